@@ -1,0 +1,48 @@
+"""Comparators shared by the parity tests (test infrastructure).
+
+Tolerances, as the workload fixes them:
+  * FP32 accumulators: |C32 - C64| <= 1e-5 * B, where B = sum_k |a_k * w_k|
+    (the same scale factors applied); where B == 0 the result must be 0.
+  * BF16 outputs: within one BF16 ulp of the oracle value rounded to nearest
+    even directly from FP64 (ordinal distance of the bit patterns, +-0 equal).
+Both refuse empty inputs and NaN, so a vacuous comparison cannot pass.
+"""
+import numpy as np
+
+REL_TOL = 1e-5
+
+
+def check_f32(c32, c64, bound, rel=REL_TOL, what=""):
+    c32 = np.asarray(c32, dtype=np.float64).ravel()
+    c64 = np.asarray(c64, dtype=np.float64).ravel()
+    bound = np.asarray(bound, dtype=np.float64).ravel()
+    assert c32.size > 0 and c32.size == c64.size == bound.size, f"{what}: empty or mismatched"
+    assert rel > 0, "degenerate tolerance"
+    assert np.all(np.isfinite(c32)), f"{what}: non-finite GPU values"
+    assert np.all(np.isfinite(c64)) and np.all(np.isfinite(bound)), f"{what}: non-finite oracle"
+    err = np.abs(c32 - c64)
+    lim = rel * bound
+    bad = np.where((bound == 0) & (c32 != 0) | (err > lim))[0]
+    assert bad.size == 0, (f"{what}: {bad.size} of {c32.size} outside 1e-5*B; first at {bad[:5]}: "
+                           f"gpu {c32[bad[:5]]} oracle {c64[bad[:5]]} B {bound[bad[:5]]}")
+    nz = bound > 0
+    return float(np.max(err[nz] / bound[nz])) if nz.any() else 0.0
+
+
+def bf16_ordinal(bits):
+    b = np.asarray(bits).astype(np.int64) & 0xFFFF
+    mag = b & 0x7FFF
+    return np.where(b & 0x8000, -mag, mag)
+
+
+def check_bf16(bits, ref_bits, what=""):
+    bits = np.asarray(bits).ravel()
+    ref_bits = np.asarray(ref_bits).ravel()
+    assert bits.size > 0 and bits.size == ref_bits.size, f"{what}: empty or mismatched"
+    nan = (bits.astype(np.int64) & 0x7FFF) > 0x7F80
+    assert not nan.any(), f"{what}: NaN in GPU output"
+    d = np.abs(bf16_ordinal(bits) - bf16_ordinal(ref_bits))
+    bad = np.where(d > 1)[0]
+    assert bad.size == 0, (f"{what}: {bad.size} of {bits.size} beyond 1 BF16 ulp; first at "
+                           f"{bad[:5]}: gpu {bits[bad[:5]]} oracle {ref_bits[bad[:5]]}")
+    return int(d.max())
