@@ -1,0 +1,102 @@
+// common.h -- device-side building blocks shared by the gfx950 GEMM kernels.
+//
+// MFMA fragment layouts used throughout (CDNA3/CDNA4 32x32 family, wave64):
+//   operand (A or B) of v_mfma_f32_32x32x16_{bf16,fp8_fp8}: lane l holds row
+//     (l % 32) of the 32-row slab, K-elements 8*(l/32) .. 8*(l/32)+7.
+//   operand of v_mfma_scale_f32_32x32x64_f8f6f4 (8-bit formats): lane l holds
+//     row (l % 32); its bytes 0..15 are K-elements 16*(l/32) .. +15 and its
+//     bytes 16..31 are K-elements 32 + 16*(l/32) .. +15.  Scale block 0
+//     (K 0..31) takes its E8M0 byte from lane (l % 32), block 1 (K 32..63)
+//     from lane 32 + (l % 32).  (Measured on gfx950 with a one-byte probe.)
+//   accumulator (16 floats): lane l holds column (l % 32); register r holds
+//     row 8*(r/4) + 4*(l/32) + (r%4).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+namespace mg {
+
+__device__ __forceinline__ f32x16 mfma_fp8(uint64_t a, uint64_t b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8((long)a, (long)b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma_bf16(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// E8M0-scaled MFMA on E4M3 operands (format code 0 for both sides)
+__device__ __forceinline__ f32x16 mfma_mx_fp8(i32x8 a, i32x8 b, f32x16 c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+
+// E2M1 -> E4M3 by bit operations (metrale_circuit hardware::exec module
+// description): a code whose sign sits in bit 7 and magnitude in bits 6..4 of
+// a byte becomes the E4M3 byte of value x 2^-6 by keeping the sign and moving
+// the magnitude down two places.  `w` holds 8 packed NVFP4 codes (byte i: low
+// nibble element 2i, high nibble element 2i+1).  Returns the 8 E4M3 bytes in
+// lane-local order [e0 e2 e4 e6 | e1 e3 e5 e7]; the matching operand of the
+// same MFMA must use the same order (a K-permutation inside one lane's slice
+// leaves every dot product unchanged).
+__device__ __forceinline__ uint64_t nvfp4x8_to_e4m3x8(uint32_t w) {
+  uint32_t odd = (w & 0x80808080u) | ((w >> 2) & 0x1C1C1C1Cu);
+  uint32_t even = ((w << 4) & 0x80808080u) | ((w << 2) & 0x1C1C1C1Cu);
+  return (uint64_t)even | ((uint64_t)odd << 32);
+}
+
+// The same lane-local order applied to 8 E4M3 bytes already in natural order
+// (activations of the W4A8 route): [b0 b2 b4 b6 | b1 b3 b5 b7].
+__device__ __forceinline__ uint64_t e4m3x8_even_odd(uint64_t v) {
+  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  uint32_t even = __builtin_amdgcn_perm(hi, lo, 0x06040200u);
+  uint32_t odd = __builtin_amdgcn_perm(hi, lo, 0x07050301u);
+  return (uint64_t)even | ((uint64_t)odd << 32);
+}
+
+// E4M3-FN byte -> BF16 bits of (its value x 64).  Exact: an E4M3 value has at
+// most 4 significant bits.  NaN bytes give a NaN.
+__device__ __forceinline__ uint32_t e4m3_x64_to_bf16(uint32_t b) {
+  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  const uint32_t normal = ((e + 126u) << 7) | (m << 4);                      // 2^(e-7) * 64
+  const uint32_t sub = __builtin_bit_cast(uint32_t, (float)m * 0.125f) >> 16;  // m/8 * 2^-6 * 64
+  uint32_t bits = e != 0u ? normal : sub;
+  bits = (e == 15u && m == 7u) ? 0x7FC0u : bits;
+  return ((b & 0x80u) << 8) | bits;
+}
+
+// E4M3-FN byte -> FP32 value (exact)
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  const float normal = __builtin_bit_cast(float, ((e + 120u) << 23) | (m << 20));
+  const float sub = (float)m * 0.001953125f;  // m * 2^-9
+  float v = e != 0u ? normal : sub;
+  v = (e == 15u && m == 7u) ? __builtin_nanf("") : v;
+  return (b & 0x80u) ? -v : v;
+}
+
+// FP32 -> BF16 bits, round to nearest even (NaN stays NaN)
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u | ((u >> 16) & 0x8000u);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// row held by accumulator register r of lane l (see the layout note above)
+__device__ __forceinline__ int acc_row(int r, int lane) {
+  return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+}
+
+}  // namespace mg

@@ -1,0 +1,62 @@
+// kernels.h -- launcher interface between the C ABI (api.cpp) and the kernels.
+// Shapes are validated by the caller; launchers only size grids and launch.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mg {
+
+struct W4A4Args {
+  const uint8_t *aq, *as;
+  const float *Sa;
+  const uint8_t *wq, *ws;
+  const float *Sw;
+  void *C;
+  int M, N, K;
+  int out_f32;
+};
+hipError_t launch_w4a4(const W4A4Args &p, hipStream_t stream);
+
+// BF16 activations against BF16 (w_nvfp4 = 0) or NVFP4 weights (w_nvfp4 = 1)
+struct Bf16Args {
+  const uint16_t *a;
+  const void *w;          // uint16 [N,K] or NVFP4 codes [N,K/2]
+  const uint8_t *ws;      // NVFP4 scales [N,K/16] (w_nvfp4 only)
+  const float *Sw;        // NVFP4 tensor scale (w_nvfp4 only)
+  void *C;
+  int M, N, K;
+  int out_f32;
+  int w_nvfp4;
+};
+hipError_t launch_bf16(const Bf16Args &p, hipStream_t stream);
+
+struct W4A8Args {
+  const uint8_t *aq;
+  const float *atok;
+  const uint8_t *wq, *ws;
+  const float *Sw;
+  void *C;
+  int M, N, K;
+  int out_f32;
+  void *work;       // split-K partials then per-tile arrival counters (launcher's layout)
+};
+size_t w4a8_workspace_bytes(int64_t M, int64_t N, int64_t K);
+int64_t w4a8_max_n();  // largest N the counter region supports
+hipError_t launch_w4a8(const W4A8Args &p, hipStream_t stream);
+
+struct MoeArgs {
+  const uint8_t *xq, *xs;
+  const int32_t *ids;
+  const float *tw;
+  int T, H, I, E, topk;
+  const uint8_t *w13q, *w13s, *w2q, *w2s;
+  uint16_t *out;
+  void *ws;
+  size_t ws_bytes;
+  uint8_t *dbg_h;
+};
+size_t moe_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk);
+hipError_t launch_moe(const MoeArgs &p, hipStream_t stream);
+
+}  // namespace mg

@@ -1,0 +1,399 @@
+// moe.hip -- MXFP8 grouped mixture-of-experts GLU on gfx950 (the MXFP8 x
+// MXFP8 -> BF16 MoE GLU of the FlashInfer swapab_cutedsl_megakernel skill
+// page, Layout section; that page names a generic MXFP8 GLU reference whose
+// computation this restates):
+//
+//   for every token t and routing slot j with expert e = ids[t,j]:
+//     [g ; u] = x_t . w13[e]^T   (K = H; rows [0,I) gate, [I,2I) up)
+//     h = silu(g) * u            (FP32)
+//     h -> MXFP8 (E8M0 per 32 along I; OCP MX rule, E4M3 saturating)
+//     y = h . w2[e]^T            (K = I)
+//     out[t] += ids weight * y   (FP32), then BF16
+//
+// Stream-ordered kernels:
+//   k_prep   zero the expert counters and the FP32 output accumulator
+//   k_count  per-expert histogram of the routing entries
+//   k_place  one workgroup per expert: row offset, stable compaction of that
+//            expert's (token, slot) entries in (token, slot) order, and its
+//            128-row tile list (so grouped GEMM grids need no host sync)
+//   k_gateup grouped GEMM on the E8M0-scaled FP8 MFMA with gathered token
+//            rows; epilogue: GLU, MXFP8 re-quantisation of h (block amax by
+//            cross-lane max), h stored in expert-sorted order
+//   k_down   grouped GEMM of sorted h rows against w2[e]; epilogue: times the
+//            routing weight, FP32 atomic add into out[t]
+//   k_cast   FP32 -> BF16
+#include "common.h"
+#include "kernels.h"
+
+namespace mg {
+namespace {
+
+constexpr int BM = 128;       // rows (routing entries) per tile
+constexpr int BNI = 64;       // intermediate columns per gate/up tile (x2 rows of w13)
+constexpr int BNH = 128;      // hidden columns per down tile
+constexpr int BK = 64;        // K per LDS stage (two 32-element scale blocks)
+constexpr int CROW = 80;      // LDS bytes per row of codes: 64 + 16 pad (bank spread)
+
+struct Layout {
+  size_t counts, meta, sorted, tile_e, tile_r, tile_n, hq, hs, outf, total;
+  int R, maxtiles;
+};
+
+size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+Layout layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk) {
+  Layout L;
+  L.R = (int)(T * topk);
+  L.maxtiles = (int)((L.R + BM - 1) / BM + E);
+  size_t o = 0;
+  L.counts = o; o += up256(sizeof(uint32_t) * (size_t)E);
+  L.meta = o;   o += up256(sizeof(int32_t) * 4);                 // [0] = number of tiles
+  L.sorted = o; o += up256(sizeof(int32_t) * (size_t)L.R);
+  L.tile_e = o; o += up256(sizeof(int32_t) * (size_t)L.maxtiles);
+  L.tile_r = o; o += up256(sizeof(int32_t) * (size_t)L.maxtiles);
+  L.tile_n = o; o += up256(sizeof(int32_t) * (size_t)L.maxtiles);
+  L.hq = o;     o += up256((size_t)L.R * (size_t)I);
+  L.hs = o;     o += up256((size_t)L.R * (size_t)(I / 32));
+  L.outf = o;   o += up256(sizeof(float) * (size_t)T * (size_t)H);
+  L.total = o;
+  return L;
+}
+
+// ---------------------------------------------------------------- routing
+__global__ void k_prep(uint32_t *counts, int E, float *outf, int64_t n) {
+  const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t step = (int64_t)gridDim.x * blockDim.x;
+  if (i0 < E) counts[i0] = 0u;
+  for (int64_t i = i0; i < n / 4; i += step) ((f32x4 *)outf)[i] = f32x4{0, 0, 0, 0};
+}
+
+__global__ void k_count(const int32_t *ids, int R, int E, uint32_t *counts) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < R) {
+    const int e = ids[i];
+    if (e >= 0 && e < E) atomicAdd(&counts[e], 1u);  // out-of-range ids are dropped
+  }
+}
+
+__global__ __launch_bounds__(256) void k_place(const int32_t *ids, int R, int E,
+                                               const uint32_t *counts, int32_t *meta,
+                                               int32_t *sorted, int32_t *tile_e,
+                                               int32_t *tile_r, int32_t *tile_n) {
+  __shared__ int s_wave[4];
+  __shared__ int s_base, s_tbase;
+  const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) {
+    int off = 0, tb = 0, tt = 0;
+    for (int q = 0; q < E; ++q) {
+      const int c = (int)counts[q];
+      const int nt = (c + BM - 1) / BM;
+      if (q < e) { off += c; tb += nt; }
+      tt += nt;
+    }
+    s_base = off;
+    s_tbase = tb;
+    if (e == 0) meta[0] = tt;
+  }
+  __syncthreads();
+  const int base = s_base, cnt = (int)counts[e];
+  // tile list of this expert
+  for (int q = tid; q * BM < cnt; q += 256) {
+    tile_e[s_tbase + q] = e;
+    tile_r[s_tbase + q] = base + q * BM;
+    tile_n[s_tbase + q] = cnt - q * BM < BM ? cnt - q * BM : BM;
+  }
+  // stable compaction of entries routed to e, in entry order (token, slot)
+  int running = 0;
+  for (int c0 = 0; c0 < R; c0 += 256) {
+    const int i = c0 + tid;
+    const bool f = i < R && ids[i] == e;
+    const uint64_t bal = __ballot(f);
+    const int before = __builtin_popcountll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) s_wave[wave] = __builtin_popcountll(bal);
+    __syncthreads();
+    int woff = 0;
+    for (int w = 0; w < wave; ++w) woff += s_wave[w];
+    const int tot = s_wave[0] + s_wave[1] + s_wave[2] + s_wave[3];
+    if (f) sorted[base + running + woff + before] = i;
+    running += tot;
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------- MX GEMM mainloop
+// A: 128 rows (row pointers per loading thread), B: 128 rows; both MXFP8
+// with K = Ktot.  Wave (wm, wn) computes rows wm*64 + [0,64) against the two
+// 32-row B slabs bsel[0], bsel[1] (LDS row offsets); acc[i][j] is the 32x32
+// block (A slab i, B slab j).
+struct MxOperandPtrs {
+  const uint8_t *a_code[2];   // this thread's two A chunk rows (code row base)
+  const uint8_t *b_code[2];
+  const uint8_t *sc_row;      // this thread's scale row (A if tid < 128, else B)
+  bool a_ok[2], b_ok[2], sc_ok;
+};
+
+__device__ __forceinline__ int crow_off(int row, int chunk) { return row * CROW + chunk * 16; }
+
+template <int NB>
+__device__ __forceinline__ void mx_mainloop(const MxOperandPtrs &ptr, int Ktot, uint8_t *lds,
+                                            const int bsel[NB], f32x16 (&acc)[2][NB]) {
+  constexpr int STAGE = 2 * BM * CROW + 2 * BM * 2;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, h = lane >> 5, l32 = lane & 31;
+  const int S = Ktot / BK;
+
+  u32x4 ra[2], rb[2];
+  uint32_t rs;
+  auto gload = [&](int s) {
+    const int k0 = s * BK;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + 256 * i, ch = c & 3;
+      ra[i] = ptr.a_ok[i] ? *(const u32x4 *)(ptr.a_code[i] + k0 + ch * 16) : u32x4{0, 0, 0, 0};
+      rb[i] = ptr.b_ok[i] ? *(const u32x4 *)(ptr.b_code[i] + k0 + ch * 16) : u32x4{0, 0, 0, 0};
+    }
+    rs = ptr.sc_ok ? (uint32_t) * (const uint16_t *)(ptr.sc_row + k0 / 32) : 0x7F7Fu;
+  };
+  auto lstore = [&](int buf) {
+    uint8_t *base = lds + buf * STAGE;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + 256 * i, row = c >> 2, ch = c & 3;
+      *(u32x4 *)(base + crow_off(row, ch)) = ra[i];
+      *(u32x4 *)(base + BM * CROW + crow_off(row, ch)) = rb[i];
+    }
+    *(uint16_t *)(base + 2 * BM * CROW + (tid >> 7) * (BM * 2) + (tid & 127) * 2) = (uint16_t)rs;
+  };
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int s = 0; s < S; ++s) {
+    const int buf = s & 1;
+    if (s + 1 < S) gload(s + 1);
+    const uint8_t *base = lds + buf * STAGE;
+    i32x8 fa[2], fb[NB];
+    int sa[2], sb[NB];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = wm * 64 + i * 32 + l32;
+      const u32x4 lo = *(const u32x4 *)(base + crow_off(row, h));
+      const u32x4 hi = *(const u32x4 *)(base + crow_off(row, 2 + h));
+      fa[i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      sa[i] = base[2 * BM * CROW + row * 2 + h];
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int row = bsel[j] + l32;
+      const u32x4 lo = *(const u32x4 *)(base + BM * CROW + crow_off(row, h));
+      const u32x4 hi = *(const u32x4 *)(base + BM * CROW + crow_off(row, 2 + h));
+      fb[j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      sb[j] = base[2 * BM * CROW + BM * 2 + row * 2 + h];
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) acc[i][j] = mfma_mx_fp8(fa[i], fb[j], acc[i][j], sa[i], sb[j]);
+    if (s + 1 < S) lstore(buf ^ 1);
+    __syncthreads();
+  }
+}
+
+constexpr int MX_LDS = 2 * (2 * BM * CROW + 2 * BM * 2);
+
+// FP32 -> E4M3-FN byte, nearest even, saturating at +-448 (NaN -> 0x7F)
+__device__ __forceinline__ uint32_t f32_to_e4m3_rne_sat(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t au = u & 0x7FFFFFFFu;
+  if (au > 0x7F800000u) return 0x7Fu;
+  const float a = __builtin_bit_cast(float, au);
+  if (!(a < 448.0f)) return sign | 0x7Eu;
+  if (a < 0.015625f) {                   // below 2^-6: steps of 2^-9
+    const uint32_t m = (uint32_t)__builtin_rintf(a * 512.0f);
+    return sign | m;                      // m == 8 is the smallest normal, code 0x08
+  }
+  const uint32_t r = (au + 0x7FFFFu + ((au >> 20) & 1u)) >> 20;  // 8-bit exp | 3-bit mantissa
+  return sign | (r - (120u << 3));
+}
+
+__device__ __forceinline__ float max32_lanes(float v) {
+  // max over the 32 lanes that share (lane / 32)
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__global__ __launch_bounds__(256) void k_gateup(MoeArgs p, const int32_t *meta,
+                                                const int32_t *sorted, const int32_t *tile_e,
+                                                const int32_t *tile_r, const int32_t *tile_n,
+                                                uint8_t *hq, uint8_t *hs) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[MX_LDS];
+  const int tile = blockIdx.y;
+  if (tile >= meta[0]) return;
+  const int e = tile_e[tile], r0 = tile_r[tile], nrows = tile_n[tile];
+  const int i0 = blockIdx.x * BNI;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1, h = lane >> 5, l32 = lane & 31;
+  const int H = p.H, I = p.I;
+
+  MxOperandPtrs ptr;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = tid + 256 * i, row = c >> 2;
+    ptr.a_ok[i] = row < nrows;
+    const int t = ptr.a_ok[i] ? sorted[r0 + row] / p.topk : 0;
+    ptr.a_code[i] = p.xq + (int64_t)t * H;
+    // B rows 0..63: gate i0+row, rows 64..127: up I+i0+row-64
+    const int brow = row < BNI ? i0 + row : I + i0 + (row - BNI);
+    ptr.b_ok[i] = true;
+    ptr.b_code[i] = p.w13q + ((int64_t)e * 2 * I + brow) * H;
+  }
+  {
+    const int row = tid & 127;
+    if (tid < 128) {
+      ptr.sc_ok = row < nrows;
+      const int t = ptr.sc_ok ? sorted[r0 + row] / p.topk : 0;
+      ptr.sc_row = p.xs + (int64_t)t * (H / 32);
+    } else {
+      ptr.sc_ok = true;
+      const int brow = row < BNI ? i0 + row : I + i0 + (row - BNI);
+      ptr.sc_row = p.w13s + ((int64_t)e * 2 * I + brow) * (H / 32);
+    }
+  }
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) acc[i][0] = acc[i][1] = f32x16{0};
+  const int bsel[2] = {wn * 32, BNI + wn * 32};  // gate slab, up slab of the same columns
+  mx_mainloop<2>(ptr, H, lds, bsel, acc);
+
+  // epilogue: h = silu(g) * u, MXFP8 block of 32 columns = this wave's 32 lanes
+  const int col = i0 + wn * 32 + l32;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = wm * 64 + i * 32 + acc_row(r, lane);
+      const float g = acc[i][0][r], u = acc[i][1][r];
+      const float hv = (g / (1.0f + expf(-g))) * u;
+      const float amax = max32_lanes(fabsf(hv));
+      uint32_t sbyte, code;
+      if (amax == 0.0f) {
+        sbyte = 0u;
+        code = 0u;
+      } else {
+        int X = (int)((__builtin_bit_cast(uint32_t, amax) >> 23) & 0xFF) - 127 - 8;
+        X = X < -127 ? -127 : (X > 127 ? 127 : X);
+        sbyte = (uint32_t)(X + 127);
+        code = f32_to_e4m3_rne_sat(__builtin_ldexpf(hv, -X));
+      }
+      if (row < nrows) {
+        const int64_t srow = r0 + row;
+        hq[srow * I + col] = (uint8_t)code;
+        if (l32 == 0) hs[srow * (I / 32) + col / 32] = (uint8_t)sbyte;
+        if (p.dbg_h) {
+          const int64_t ent = sorted[srow];
+          uint8_t *d = p.dbg_h + ent * (int64_t)(I + I / 32);
+          d[col] = (uint8_t)code;
+          if (l32 == 0) d[I + col / 32] = (uint8_t)sbyte;
+        }
+      }
+    }
+}
+
+__global__ __launch_bounds__(256) void k_down(MoeArgs p, const int32_t *meta, const int32_t *sorted,
+                                              const int32_t *tile_e, const int32_t *tile_r,
+                                              const int32_t *tile_n, const uint8_t *hq,
+                                              const uint8_t *hs, float *outf) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[MX_LDS];
+  const int tile = blockIdx.y;
+  if (tile >= meta[0]) return;
+  const int e = tile_e[tile], r0 = tile_r[tile], nrows = tile_n[tile];
+  const int n0 = blockIdx.x * BNH;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31;
+  const int H = p.H, I = p.I;
+
+  MxOperandPtrs ptr;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = tid + 256 * i, row = c >> 2;
+    ptr.a_ok[i] = row < nrows;
+    ptr.a_code[i] = hq + (int64_t)(r0 + (row < nrows ? row : 0)) * I;
+    ptr.b_ok[i] = n0 + row < H;
+    ptr.b_code[i] = p.w2q + ((int64_t)e * H + n0 + row) * I;
+  }
+  {
+    const int row = tid & 127;
+    if (tid < 128) {
+      ptr.sc_ok = row < nrows;
+      ptr.sc_row = hs + (int64_t)(r0 + (row < nrows ? row : 0)) * (I / 32);
+    } else {
+      ptr.sc_ok = n0 + row < H;
+      ptr.sc_row = p.w2s + ((int64_t)e * H + n0 + row) * (I / 32);
+    }
+  }
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) acc[i][0] = acc[i][1] = f32x16{0};
+  const int bsel[2] = {wn * 64, wn * 64 + 32};
+  mx_mainloop<2>(ptr, I, lds, bsel, acc);
+
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = wm * 64 + i * 32 + acc_row(r, lane);
+      if (row >= nrows) continue;
+      const int ent = sorted[r0 + row];
+      const int t = ent / p.topk;
+      const float w = p.tw[ent];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int n = n0 + wn * 64 + j * 32 + l32;
+        if (n < H) unsafeAtomicAdd(&outf[(int64_t)t * H + n], acc[i][j][r] * w);
+      }
+    }
+}
+
+__global__ void k_cast(const float *outf, uint16_t *out, int64_t n) {
+  const int64_t step = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n / 4; i += step) {
+    const f32x4 v = ((const f32x4 *)outf)[i];
+    u32x2 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    ((u32x2 *)out)[i] = o;
+  }
+}
+
+}  // namespace
+
+size_t moe_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk) {
+  return layout(T, H, I, E, topk).total;
+}
+
+hipError_t launch_moe(const MoeArgs &p, hipStream_t stream) {
+  const Layout L = layout(p.T, p.H, p.I, p.E, p.topk);
+  char *w = (char *)p.ws;
+  uint32_t *counts = (uint32_t *)(w + L.counts);
+  int32_t *meta = (int32_t *)(w + L.meta);
+  int32_t *sorted = (int32_t *)(w + L.sorted);
+  int32_t *tile_e = (int32_t *)(w + L.tile_e);
+  int32_t *tile_r = (int32_t *)(w + L.tile_r);
+  int32_t *tile_n = (int32_t *)(w + L.tile_n);
+  uint8_t *hq = (uint8_t *)(w + L.hq);
+  uint8_t *hs = (uint8_t *)(w + L.hs);
+  float *outf = (float *)(w + L.outf);
+  const int64_t TH = (int64_t)p.T * p.H;
+
+  hipLaunchKernelGGL(k_prep, dim3(1024), dim3(256), 0, stream, counts, p.E, outf, TH);
+  hipLaunchKernelGGL(k_count, dim3((L.R + 255) / 256), dim3(256), 0, stream, p.ids, L.R, p.E, counts);
+  hipLaunchKernelGGL(k_place, dim3(p.E), dim3(256), 0, stream, p.ids, L.R, p.E, counts, meta,
+                     sorted, tile_e, tile_r, tile_n);
+  hipLaunchKernelGGL(k_gateup, dim3(p.I / BNI, L.maxtiles), dim3(256), 0, stream, p, meta, sorted,
+                     tile_e, tile_r, tile_n, hq, hs);
+  hipLaunchKernelGGL(k_down, dim3((p.H + BNH - 1) / BNH, L.maxtiles), dim3(256), 0, stream, p,
+                     meta, sorted, tile_e, tile_r, tile_n, hq, hs, outf);
+  hipLaunchKernelGGL(k_cast, dim3(1024), dim3(256), 0, stream, outf, p.out, TH);
+  return hipGetLastError();
+}
+
+}  // namespace mg

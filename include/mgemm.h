@@ -1,0 +1,210 @@
+/*
+ * mgemm.h -- C ABI of the MI355X (gfx950) block-scaled TN GEMM library.
+ *
+ * One operation, several declared formats:
+ *
+ *     C[M,N] = A[M,K] . W[N,K]^T      (FP32 accumulation, BF16 output)
+ *
+ * All operands are K-contiguous ("TN"): A is [M,K] row-major, W is [N,K]
+ * row-major, C is [M,N] row-major.  The declared formats and how each one
+ * executes follow the metrale_circuit "hardware::exec" module documentation
+ * (module description; entries exec_of, fp4_fallback, kind_of, node_exec,
+ * pair_name): the activation format picks the matrix instruction, NVFP4
+ * operands on a device without an NVFP4 block-scale MMA go through the exact
+ * E2M1 -> E4M3 conversion onto the FP8 MMA with the group scales applied in
+ * FP32 per K=16 step, and a pair with no native or exact path has no path --
+ * it is never re-run at a wider format.
+ *
+ * Storage formats
+ *   BF16        uint16 bits, [R,K].
+ *   NVFP4       codes uint8 [R,K/2], element 2i in the LOW nibble of byte i,
+ *               element 2i+1 in the high nibble (E2M1: sign bit 3, exponent
+ *               bits 2..1, mantissa bit 0); scales uint8 [R,K/16] E4M3-FN, one
+ *               per 16 consecutive K-elements; one FP32 tensor scale S (a
+ *               DEVICE pointer to one float).  Value = e2m1 * e4m3 * S.
+ *   FP8 token   E4M3-FN bytes [M,K] and one FP32 scale per row (device
+ *               pointer, [M]).  Value = e4m3 * s[m].
+ *   MXFP8       E4M3-FN bytes [R,K] and E8M0 bytes [R,K/32] (2^(x-127)).
+ *
+ * Calling conventions (every GEMM entry point)
+ *   - Pointers are DEVICE pointers of the current HIP device unless stated;
+ *     the caller owns every buffer.  The library allocates nothing for the
+ *     GEMMs and keeps no state between calls; calls are reentrant.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *     default stream).  C is fully overwritten (no beta).
+ *   - out_f32 = 0: C is BF16 (round to nearest even from the FP32 result).
+ *     out_f32 = 1: C is FP32 (the accumulator after the global scales).
+ *   - K must be a positive multiple of 32; M, N must be positive.  Base
+ *     pointers must be 16-byte aligned.
+ *   - Data values are not validated (a NaN scale byte gives NaN results).
+ *
+ * Return codes: 0 on success, a negative MGEMM_ERR_* otherwise;
+ * mgemm_status_string() names them.  Argument errors are detected on the
+ * host before anything is enqueued.
+ */
+#ifndef MGEMM_H
+#define MGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* declared storage formats */
+enum {
+  MGEMM_FMT_BF16 = 0,
+  MGEMM_FMT_NVFP4 = 1,
+  MGEMM_FMT_FP8_E4M3_TOKEN = 2,
+  MGEMM_FMT_MXFP8 = 3
+};
+
+/* execution kind of one (weight, activation) pair on a device */
+enum { MGEMM_EXEC_NATIVE = 0, MGEMM_EXEC_FP8_EXACT = 1, MGEMM_EXEC_NOPATH = 2 };
+
+/* the matrix instruction that carries the declared formats */
+enum {
+  MGEMM_MMA_NONE = 0,
+  MGEMM_MMA_BF16 = 1,        /* v_mfma_f32_32x32x16_bf16 */
+  MGEMM_MMA_FP8 = 2,         /* v_mfma_f32_32x32x16_fp8_fp8, one K=16 group each */
+  MGEMM_MMA_MX_F8F6F4 = 3    /* v_mfma_scale_f32_32x32x64_f8f6f4, E8M0 per 32 */
+};
+
+/* why a pair runs the way it does (0 = native) */
+enum {
+  MGEMM_REASON_NONE = 0,
+  MGEMM_REASON_NO_INSTRUCTION = 1,        /* no instruction can carry the pair exactly */
+  MGEMM_REASON_NO_KERNEL = 2,             /* the library compiles no kernel for the pair */
+  MGEMM_REASON_NO_NVFP4_BLOCKSCALE_MMA = 3, /* the FP4 MMA here is MX-scaled only */
+  MGEMM_REASON_NO_SINGLE_MMA = 4,         /* NVFP4 weights under FP8 activations */
+  MGEMM_REASON_UNSUPPORTED_DEVICE = 5     /* not a gfx950 device */
+};
+
+typedef struct {
+  int kind;   /* MGEMM_EXEC_* */
+  int mma;    /* MGEMM_MMA_* */
+  int reason; /* MGEMM_REASON_* */
+} mgemm_plan_t;
+
+/* status codes */
+enum {
+  MGEMM_OK = 0,
+  MGEMM_ERR_INVALID_ARG = -1, /* NULL pointer, bad enum, misaligned pointer */
+  MGEMM_ERR_SHAPE = -2,       /* M/N/K not positive, K % 32 != 0, size overflow */
+  MGEMM_ERR_NOPATH = -3,      /* the plan for this pair on this device is NOPATH */
+  MGEMM_ERR_WORKSPACE = -4,   /* workspace NULL or smaller than required */
+  MGEMM_ERR_HIP = -5          /* a HIP runtime call or launch failed */
+};
+
+/* --------------------------------------------------------------- planning */
+
+/* How device `device` executes a node with weight format w_fmt under
+   activation format a_fmt (hardware::exec docs: exec_of, fp4_fallback,
+   kind_of, node_exec).  Host only; enqueues nothing.  On gfx950:
+     BF16 x BF16   -> NATIVE, BF16 MMA
+     NVFP4 w, BF16 a -> NATIVE, BF16 MMA (weights widened in registers, exact)
+     NVFP4 w, FP8 a  -> FP8_EXACT, FP8 MMA (reason NO_SINGLE_MMA)
+     NVFP4 w, NVFP4 a -> FP8_EXACT, FP8 MMA (reason NO_NVFP4_BLOCKSCALE_MMA)
+     MXFP8 x MXFP8 -> NATIVE, MX f8f6f4 MMA
+     anything else -> NOPATH.  Any other device -> NOPATH (UNSUPPORTED_DEVICE).
+   Returns 0, MGEMM_ERR_INVALID_ARG (bad enum / NULL out), MGEMM_ERR_HIP. */
+int mgemm_plan(int device, int w_fmt, int a_fmt, mgemm_plan_t *out);
+
+/* The same decision for a named architecture (e.g. "gfx950:sramecc+:xnack-");
+   needs no GPU.  Only the part before the first ':' is compared. */
+int mgemm_plan_arch(const char *gcn_arch, int w_fmt, int a_fmt, mgemm_plan_t *out);
+
+/* The declared pair as text, "W<bits>A<bits>" (hardware::exec docs:
+   pair_name): BF16 = 16, NVFP4 = 4, FP8 = 8, MXFP8 = 8, e.g. "W4A16".
+   Writes a NUL-terminated string into buf (host memory, len bytes).
+   Returns the string length, or MGEMM_ERR_INVALID_ARG. */
+int mgemm_pair_name(int w_fmt, int a_fmt, char *buf, size_t len);
+
+/* ------------------------------------------------------------------ GEMMs */
+
+/* W16A16: C = A . W^T with BF16 A [M,K] and W [N,K] on the BF16 MFMA,
+   FP32 accumulation (the H3 FFN down-projection of RL-Kernel PR #535:
+   BF16 MMA tiles, FP32 accumulation, BF16 epilogue). */
+int mgemm_bf16(const void *A, const void *W, void *C, int64_t M, int64_t N,
+               int64_t K, int out_f32, void *stream);
+
+/* W4A16: BF16 activations A [M,K] under NVFP4 weights (Wq [N,K/2],
+   Ws [N,K/16], Sw device float*).  Each weight element e2m1*e4m3 is widened
+   to BF16 in registers (exact: at most 6 significant bits) and run on the
+   BF16 MFMA; Sw is applied in the epilogue (hardware::exec docs, module
+   description: BF16 activations take the BF16 MMA with the weight widened). */
+int mgemm_w4a16(const void *A, const void *Wq, const void *Ws, const float *Sw,
+                void *C, int64_t M, int64_t N, int64_t K, int out_f32, void *stream);
+
+/* W4A8: FP8 E4M3 activations Aq [M,K] with per-token FP32 scales a_tok [M]
+   under NVFP4 weights.  Exact E4M3 route (hardware::exec docs, exec_of):
+   weight codes converted by the E2M1 -> E4M3 bit identity, one FP8 MFMA per
+   16-element group, the group scale (times 64) applied in FP32 per group,
+   a_tok[m] * Sw in the epilogue.  The decode kernel splits K over
+   workgroups and needs a workspace: `ws` device memory of at least
+   mgemm_workspace_bytes(MGEMM_OP_W4A8, M, N, K, ...) bytes (when that is 0,
+   ws may be NULL).  The workspace must be zero-filled before its first use;
+   every call leaves its arrival counters at zero again, so one workspace
+   serves any later call of the same or smaller size.  Calls that share a
+   workspace must be ordered on one stream.  Split partials are reduced in a
+   fixed order: results are run-to-run bit-identical.  M is processed in
+   slices of 128 rows; N may be at most 524288. */
+int mgemm_w4a8(const void *Aq, const float *a_tok, const void *Wq, const void *Ws,
+               const float *Sw, void *C, int64_t M, int64_t N, int64_t K, int out_f32,
+               void *ws, size_t ws_bytes, void *stream);
+
+/* W4A4: NVFP4 activations (Aq [M,K/2], As [M,K/16], Sa) under NVFP4 weights.
+   Exact E4M3 route (hardware::exec docs, module description and
+   fp4_fallback): both operands' codes converted by the E2M1 -> E4M3 bit
+   identity, one FP8 MFMA per 16-element group with a zero accumulator, the
+   product of the two group scales (each times 64) applied by one FP32
+   fused multiply-add per group, groups in ascending K; Sa * Sw in the
+   epilogue.  Each group term is exact in FP32; only the cross-group FP32
+   additions round. */
+int mgemm_w4a4(const void *Aq, const void *As, const float *Sa, const void *Wq,
+               const void *Ws, const float *Sw, void *C, int64_t M, int64_t N,
+               int64_t K, int out_f32, void *stream);
+
+/* MXFP8 grouped mixture-of-experts GLU (FlashInfer swapab_cutedsl_megakernel
+   skill page, Layout section: an MXFP8 GLU MoE with an MXFP8 x MXFP8 -> BF16
+   backend).  Inputs: xq [T,H] E4M3 and xs [T,H/32] E8M0 tokens; topk_ids
+   [T,topk] int32 in [0,E) (entries outside that range are dropped); topk_w [T,topk] FP32 routing weights; w13q
+   [E,2I,H] E4M3 with w13s [E,2I,H/32] (rows [0,I) gate, [I,2I) up); w2q
+   [E,H,I] with w2s [E,H,I/32].  Per token t and slot j with expert e:
+     [g;u] = x_t . w13[e]^T;  h = silu(g) * u (FP32);
+     h is re-quantised to MXFP8 (E8M0 per 32 along I, OCP MX rule);
+     y = h . w2[e]^T;  out[t] = sum_j topk_w[t,j] * y  (FP32), then BF16.
+   out: [T,H] BF16.  ws: device workspace of at least
+   mgemm_workspace_bytes(MGEMM_OP_MOE, ...) bytes; its counters are zeroed on
+   `stream` by the call itself before use.  dbg_h: NULL, or a device buffer of
+   T*topk*(I + I/32) bytes that receives each (token, slot) row of the
+   re-quantised h (I code bytes then I/32 scale bytes) at row t*topk + j.
+   H and I must be multiples of 64, topk in [1,16], E in [1,1024], T <= 2^24.
+   The FP32 combine is order-dependent (atomic adds): results agree with the
+   fixed-order sum to FP32 rounding, not bit for bit. */
+int mgemm_moe_mxfp8_glu(const void *xq, const void *xs, const int32_t *topk_ids,
+                        const float *topk_w, int64_t T, int64_t H, int64_t I,
+                        int64_t E, int64_t topk, const void *w13q, const void *w13s,
+                        const void *w2q, const void *w2s, void *out, void *ws,
+                        size_t ws_bytes, void *dbg_h, void *stream);
+
+/* workspace sizes */
+enum { MGEMM_OP_BF16 = 0, MGEMM_OP_W4A16 = 1, MGEMM_OP_W4A8 = 2, MGEMM_OP_W4A4 = 3,
+       MGEMM_OP_MOE = 4 };
+/* Bytes of device workspace an op needs for these sizes (0 if none).  For the
+   GEMMs pass (M, N, K) and zeros; for the MoE pass (T, H, I, E, topk) in the
+   T.. arguments.  Returns 0 for unknown ops or invalid sizes as well. */
+size_t mgemm_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int64_t T,
+                             int64_t H, int64_t I, int64_t E, int64_t topk);
+
+/* static text for a status code */
+const char *mgemm_status_string(int status);
+
+/* library version string */
+const char *mgemm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MGEMM_H */
