@@ -1,0 +1,271 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-scaled TN GEMM library on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--quick]
+
+One step is one call of the headline path: the W4A4 NVFP4 TN GEMM
+C[8192,5376] = A[8192,14336] . W[5376,14336]^T (NVFP4 E2M1 codes, E4M3 scales
+per 16, FP32 tensor scales; exact E2M1->E4M3 conversion onto the FP8 MFMA,
+per-16 FP32 scale step, BF16 output), inputs resident in HBM.  W warmup steps
+run untimed, then exactly K steps are timed between two device
+synchronisations with HIP events on the stream the kernel runs on.  `value`
+is TFLOP/s = 2*M*N*K / time per step.
+
+The same JSON line also carries: the roofline of that kernel, the FP64 CPU
+oracle timed on the host on a bounded sample of the same workload
+(`cpu_baseline`), a sampled parity check of the timed output against the
+oracle, the W4A8 swap-AB decode shapes (M = 1, 8, 32, 128; GB/s against the
+HBM roofline, weights rotated over 8 copies so the 256 MB Infinity Cache
+cannot serve them), and the BF16 and MXFP8-MoE configurations.
+
+Only one GPU is supported: --gpus N with N > 1 exits with a message.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+M, N, K = 8192, 5376, 14336
+PEAK = {"bf16": 2500.0, "fp8": 5000.0, "fp32": 157.3, "hbm": 8000.0}  # TFLOP/s, GB/s
+# plain FP32 vector FMA without packed instructions: 256 CU x 4 SIMD x 16 lanes x 2 flop x 2.4 GHz
+PEAK_VALU_F32 = 78.6
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--quick", action="store_true", help="headline kernel only")
+    ap.add_argument("--only", default="", help="w4a4|w4a8|bf16|moe (profiling runs)")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="also run one plain copy kernel of this many MiB (counter calibration)")
+    return ap.parse_args()
+
+
+def src_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "block_scaled_precision_tn_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel_file, key):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        d = json.load(open(p))[key]
+    except (OSError, KeyError, ValueError):
+        return None
+    if d.get("src_hash") != src_hash(kernel_file, "common.h"):
+        return None
+    return d.get("bytes_per_launch")
+
+
+def timed(torch, fn, steps, warmup, stream):
+    for _ in range(warmup):
+        fn(0)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        fn(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps  # ms per call
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
+              "this library has no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import block_scaled_precision_tn_amd as mg
+    import synth
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    mg.load()  # the HIP library must be built: there is no fallback
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    out = {}
+
+    def todev(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    def f32(v):
+        return torch.tensor([float(v)], dtype=torch.float32, device=dev)
+
+    # ------------------------------------------------------ W4A4 (headline)
+    run_w4a4 = args.only in ("", "w4a4")
+    if run_w4a4:
+        t0 = time.time()
+        inp = synth.w4a4(M, N, K, seed=0)
+        gen_s = time.time() - t0
+        d = {k: todev(v) for k, v in inp.items() if isinstance(v, np.ndarray) and v.ndim}
+        Sa, Sw = f32(inp["Sa"]), f32(inp["Sw"])
+        C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        call = lambda i: mg.mgemm_w4a4(d["aq"], d["as_"], Sa, d["wq"], d["ws"], Sw, C)  # noqa: E731
+        ms = timed(torch, call, args.steps, args.warmup, stream)
+        flops = 2.0 * M * N * K
+        tflops = flops / (ms * 1e-3) / 1e12
+        groups = M * N * (K // 16)
+        traffic = traffic_for("gemm_w4a4.hip", "w4a4_m8192")
+        out["w4a4"] = dict(ms=ms, tflops=tflops, gen_s=gen_s)
+        out["roofline"] = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK["fp8"],
+                           "unit": "TFLOP/s", "frac": round(tflops / PEAK["fp8"], 4),
+                           "traffic": traffic}
+        # the per-16 FP32 scale step: one fused multiply-add per output per group
+        alu = 2.0 * groups / (ms * 1e-3) / 1e12
+        out["alu_roofline"] = {"what": "per-group FP32 scale FMA (1 per output per 16 K)",
+                               "achieved": round(alu, 2), "peak": PEAK_VALU_F32, "unit": "TFLOP/s",
+                               "frac": round(alu / PEAK_VALU_F32, 4)}
+        # sampled parity of the timed output against the oracle (bench sanity)
+        rng = np.random.default_rng(1)
+        pm, pn = rng.integers(0, M, 64), rng.integers(0, N, 64)
+        cbits = C.view(torch.int16)[torch.from_numpy(pm).to(dev), torch.from_numpy(pn).to(dev)]
+        out["_sample"] = (inp, pm, pn, cbits.cpu().numpy().view(np.uint16))
+        del d, C
+        torch.cuda.empty_cache()
+
+    # --------------------------------------------------- W4A8 decode shapes
+    if args.only in ("", "w4a8") and not args.quick:
+        w = synth.w4a8(1, N, K, seed=0)  # the weight tensor is shared by every M
+        copies = 8  # 8 x 43.4 MB > 256 MB Infinity Cache
+        wq = [todev(w["wq"]) for _ in range(copies)]
+        ws = [todev(w["ws"]) for _ in range(copies)]
+        Sw = f32(w["Sw"])
+        dec = []
+        for Mi in (1, 8, 32, 128):
+            a = synth.normal((Mi, K), 1.0, Mi, synth.ROLE_A)
+            aq, atok = synth.quant_fp8_token(a)
+            aq, atok = todev(aq), todev(atok)
+            Cd = torch.empty((Mi, N), dtype=torch.bfloat16, device=dev)
+            wsp = mg.workspace(mg.mgemm_workspace_bytes(mg.OP_W4A8, Mi, N, K), "w4a8")
+            call = lambda i: mg.mgemm_w4a8(aq, atok, wq[i % copies], ws[i % copies], Sw, Cd, ws=wsp)  # noqa: E731
+            ms = timed(torch, call, max(args.steps, 40), args.warmup, stream)
+            nbytes = N * K // 2 + N * K // 16 + Mi * K + 4 * Mi + 2 * Mi * N
+            gbps = nbytes / (ms * 1e-3) / 1e9
+            dec.append({"M": Mi, "us": round(ms * 1e3, 2), "GBps": round(gbps, 1),
+                        "frac_hbm": round(gbps / PEAK["hbm"], 4), "bytes": nbytes,
+                        "tflops": round(2.0 * Mi * N * K / (ms * 1e-3) / 1e12, 2)})
+        out["decode"] = dec
+        del wq, ws
+        torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------------ BF16
+    if args.only in ("", "bf16") and not args.quick:
+        Mb = 4096
+        b = synth.bf16(Mb, N, K, seed=0)
+        A = todev(b["a"].view(np.int16)).view(torch.bfloat16)
+        W = todev(b["w"].view(np.int16)).view(torch.bfloat16)
+        Cb = torch.empty((Mb, N), dtype=torch.bfloat16, device=dev)
+        ms = timed(torch, lambda i: mg.mgemm_bf16(A, W, Cb), args.steps, args.warmup, stream)
+        tf = 2.0 * Mb * N * K / (ms * 1e-3) / 1e12
+        ms_t = timed(torch, lambda i: torch.matmul(A, W.t()), args.steps, args.warmup, stream)
+        tf_t = 2.0 * Mb * N * K / (ms_t * 1e-3) / 1e12
+        out["bf16"] = {"M": Mb, "N": N, "K": K, "ms": round(ms, 4), "tflops": round(tf, 1),
+                       "frac_bf16_peak": round(tf / PEAK["bf16"], 4),
+                       "torch_matmul_tflops": round(tf_t, 1)}
+        del A, W, Cb
+        torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------------- MoE
+    if args.only in ("", "moe") and not args.quick:
+        T, H, I, E, topk = 4096, 4096, 1536, 64, 8
+        m = synth.moe(T, H, I, E, topk, seed=0)
+        dm = {k: todev(v) for k, v in m.items()}
+        o = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        wsp = mg.workspace(mg.mgemm_workspace_bytes(mg.OP_MOE, T=T, H=H, I=I, E=E, topk=topk), "moe")
+        call = lambda i: mg.mgemm_moe_mxfp8_glu(dm["xq"], dm["xs"], dm["ids"], dm["tw"], dm["w13q"],  # noqa: E731
+                                                dm["w13s"], dm["w2q"], dm["w2s"], o, ws=wsp)
+        ms = timed(torch, call, max(3, args.steps // 2), min(args.warmup, 3), stream)
+        fl = 2.0 * T * topk * (H * 2 * I + I * H)
+        tf = fl / (ms * 1e-3) / 1e12
+        out["moe"] = {"T": T, "H": H, "I": I, "E": E, "topk": topk, "ms": round(ms, 3),
+                      "tflops": round(tf, 1), "frac_fp8_peak": round(tf / PEAK["fp8"], 4)}
+        del dm, o
+        torch.cuda.empty_cache()
+
+    if args.copy_calib_mib:
+        n = args.copy_calib_mib * (1 << 20) // 4
+        x = torch.ones(n, dtype=torch.float32, device=dev)
+        y = torch.empty_like(x)
+        torch.mul(x, 1.0, out=y)  # reads n*4 bytes, writes n*4 bytes
+        torch.cuda.synchronize()
+
+    # ----------------------------------------------------- CPU baseline leg
+    cpu = None
+    par = None
+    if run_w4a4 and not args.no_cpu_baseline:
+        import oracle
+        from oracle import NVFP4, Operand
+        inp, pm, pn, gbits = out.pop("_sample")
+        A_op = Operand(NVFP4, inp["aq"], inp["as_"], tscale=float(inp["Sa"]))
+        W_op = Operand(NVFP4, inp["wq"], inp["ws"], tscale=float(inp["Sw"]))
+        cores = max(1, min(os.cpu_count() or 1, 16))
+        c64, b64 = oracle.gemm_points(A_op, W_op, pm, pn, nthreads=cores)
+        ref = oracle.bf16_rne(c64)
+        o_ord = lambda b: np.where(b & 0x8000, -(b & 0x7FFF).astype(np.int64), (b & 0x7FFF).astype(np.int64))  # noqa: E731
+        par = {"points": int(len(pm)), "max_bf16_ulp": int(np.max(np.abs(o_ord(gbits) - o_ord(ref))))}
+        # calibrate, then time ~15 s of oracle work on the first output rows
+        rng = np.random.default_rng(2)
+        t0 = time.time()
+        oracle.gemm_points(A_op, W_op, rng.integers(0, M, 256), rng.integers(0, N, 256), nthreads=cores)
+        per_pt = (time.time() - t0) / 256
+        npts = int(max(256, min(2_000_000, 15.0 / max(per_pt, 1e-9))))
+        sm, sn = np.divmod(np.arange(npts, dtype=np.int64), N)
+        t0 = time.time()
+        oracle.gemm_points(A_op, W_op, sm, sn, nthreads=cores)
+        dt = time.time() - t0
+        cpu = {"value": round(npts * 2.0 * K / dt / 1e12, 8), "unit": "TFLOP/s", "cores": cores,
+               "kind": "oracle", "sample": f"{npts} outputs (rows 0..{int(sm[-1])} of C) of the "
+               f"W4A4 M={M} K={K} N={N} workload, FP64, {dt:.1f} s"}
+    else:
+        out.pop("_sample", None)
+
+    w = out.get("w4a4")
+    line = {
+        "metric": "TFLOP/s + % MFMA peak, W4A4 NVFP4 M=8192 K=14336 N=5376; decode GB/s",
+        "value": round(w["tflops"], 2) if w else None,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(w["ms"], 4) if w else None,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8",
+        "data": "synthetic",
+        "config": {"workload": f"W4A4 NVFP4 TN GEMM M={M} K={K} N={N} (FFN down projection shape)",
+                   "M": M, "N": N, "K": K, "parallelism": "single GPU"},
+        "roofline": out.get("roofline"),
+        "cpu_baseline": cpu,
+        "alu_roofline": out.get("alu_roofline"),
+        "parity_sample": par,
+        "decode": out.get("decode"),
+        "bf16": out.get("bf16"),
+        "moe": out.get("moe"),
+        "device": torch.cuda.get_device_properties(0).gcnArchName,
+        "kernel_src": src_hash("gemm_w4a4.hip", "common.h"),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

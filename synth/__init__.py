@@ -18,13 +18,62 @@ BF16, the FlashInfer ``swapab_cutedsl_megakernel`` skill page for MXFP8):
   to [-127, 127], E8M0 byte ``X+127`` (0 for an all-zero block), codes
   ``RNE_E4M3(v/2^X)`` saturating at 448.
 
-All randomness comes from ``numpy.random.default_rng`` streams spawned from one
-``SeedSequence(seed)``, one child per tensor role, so every tensor is
-reproducible on its own.
+Normal samples come from a counter-based generator (SplitMix64 over a key
+derived from (seed, tensor role) and the element index, Box-Muller pairs), so
+every tensor is reproducible on its own and independent of thread count; the
+bulk work runs in ``synth.c`` (multi-threaded C).  The small random choices
+(outlier columns, routing logits) use ``numpy.random.default_rng`` streams
+spawned from ``SeedSequence(seed)``.  The numpy encoders below (``np_*``) are a
+second, independent implementation kept to cross-check the C ones.
 """
 from __future__ import annotations
 
+import ctypes as C
+import os
+import subprocess
+
 import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "synth.c")
+_LIB = os.path.join(_HERE, "libsynth.so")
+_lib = None
+
+
+def build() -> str:
+    tmp = _LIB + ".tmp"
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-D_DEFAULT_SOURCE", "-fPIC", "-shared",
+                           "-Wall", _SRC, "-o", tmp, "-lm", "-lpthread"])
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build()
+    lib = C.CDLL(_LIB)
+    vp, i64, i32 = C.c_void_p, C.c_int64, C.c_int
+    lib.syn_key.restype = C.c_uint64
+    lib.syn_key.argtypes = [C.c_uint64, C.c_uint64]
+    lib.syn_normal.restype = None
+    lib.syn_normal.argtypes = [C.c_uint64, C.c_float, vp, i64, i32]
+    lib.syn_quant_nvfp4.restype = C.c_float
+    lib.syn_quant_nvfp4.argtypes = [vp, i64, i64, vp, vp, i32]
+    lib.syn_quant_fp8_token.restype = None
+    lib.syn_quant_fp8_token.argtypes = [vp, i64, i64, vp, vp, i32]
+    lib.syn_quant_mxfp8.restype = None
+    lib.syn_quant_mxfp8.argtypes = [vp, i64, vp, vp, i32]
+    lib.syn_to_bf16.restype = None
+    lib.syn_to_bf16.argtypes = [vp, i64, vp, i32]
+    _lib = lib
+    return lib
+
+
+def _nth():
+    return max(1, min(os.cpu_count() or 1, 16))
 
 # one child stream per tensor role
 ROLE_A, ROLE_W, ROLE_OUTLIER, ROLE_LOGITS, ROLE_W2 = 0, 1, 2, 3, 4
@@ -39,10 +88,10 @@ def role_rng(seed: int, role: int) -> np.random.Generator:
 
 
 def normal(shape, std: float, seed: int, role: int) -> np.ndarray:
-    """FP32 samples of N(0, std^2)."""
-    x = role_rng(seed, role).standard_normal(size=shape, dtype=np.float32)
-    if std != 1.0:
-        x *= np.float32(std)
+    """FP32 samples of N(0, std^2) (counter-based, see the module note)."""
+    x = np.empty(shape, dtype=np.float32)
+    lib = _load()
+    lib.syn_normal(lib.syn_key(seed, role), float(std), x.ctypes.data, x.size, _nth())
     return x
 
 
@@ -58,7 +107,7 @@ def with_outliers(a: np.ndarray, cols: np.ndarray, factor: float = 20.0) -> np.n
 
 
 # ----------------------------------------------------------------- encoders
-def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+def np_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round FP32 to BF16 (nearest, ties to even); returns uint16 bits."""
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
     lsb = (u >> 16) & 1
@@ -109,7 +158,7 @@ def _e2m1_encode(x: np.ndarray) -> np.ndarray:
     return (idx.astype(np.uint8) | np.where(np.signbit(x) & (idx > 0), 8, 0).astype(np.uint8))
 
 
-def quant_nvfp4(x: np.ndarray, chunk_rows: int = 1024):
+def np_quant_nvfp4(x: np.ndarray, chunk_rows: int = 1024):
     """FP32 [R,K] -> (codes uint8 [R,K/2], scales uint8 [R,K/16], S float32)."""
     R, K = x.shape
     assert K % 16 == 0
@@ -132,7 +181,7 @@ def quant_nvfp4(x: np.ndarray, chunk_rows: int = 1024):
     return codes, scales, S
 
 
-def quant_fp8_token(a: np.ndarray, chunk_rows: int = 1024):
+def np_quant_fp8_token(a: np.ndarray, chunk_rows: int = 1024):
     """FP32 [M,K] -> (E4M3 bytes [M,K], per-token FP32 scale [M])."""
     M, K = a.shape
     amax = np.abs(a).max(axis=1).astype(np.float32) if K else np.zeros(M, np.float32)
@@ -144,7 +193,7 @@ def quant_fp8_token(a: np.ndarray, chunk_rows: int = 1024):
     return q, s
 
 
-def quant_mxfp8(v: np.ndarray, chunk_rows: int = 512):
+def np_quant_mxfp8(v: np.ndarray, chunk_rows: int = 512):
     """FP32 [..., K] -> (E4M3 bytes [..., K], E8M0 bytes [..., K/32])."""
     shape = v.shape
     K = shape[-1]
@@ -162,6 +211,46 @@ def quant_mxfp8(v: np.ndarray, chunk_rows: int = 512):
         c = _e4m3_encode(np.ldexp(blk, -X[..., None]))
         codes[r0:r0 + chunk_rows] = c.reshape(-1, K)
     return codes.reshape(shape), scales.reshape(shape[:-1] + (K // 32,))
+
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round FP32 to BF16 (nearest, ties to even); returns uint16 bits."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, np.uint16)
+    _load().syn_to_bf16(x.ctypes.data, x.size, out.ctypes.data, _nth())
+    return out
+
+
+def quant_nvfp4(x: np.ndarray):
+    """FP32 [R,K] -> (codes uint8 [R,K/2], scales uint8 [R,K/16], S float32)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    R, K = x.shape
+    assert K % 16 == 0
+    codes = np.empty((R, K // 2), np.uint8)
+    scales = np.empty((R, K // 16), np.uint8)
+    S = _load().syn_quant_nvfp4(x.ctypes.data, R, K, codes.ctypes.data, scales.ctypes.data, _nth())
+    return codes, scales, np.float32(S)
+
+
+def quant_fp8_token(a: np.ndarray):
+    """FP32 [M,K] -> (E4M3 bytes [M,K], per-token FP32 scale [M])."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    M, K = a.shape
+    q = np.empty((M, K), np.uint8)
+    s = np.empty(M, np.float32)
+    _load().syn_quant_fp8_token(a.ctypes.data, M, K, q.ctypes.data, s.ctypes.data, _nth())
+    return q, s
+
+
+def quant_mxfp8(v: np.ndarray):
+    """FP32 [..., K] -> (E4M3 bytes [..., K], E8M0 bytes [..., K/32])."""
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    K = v.shape[-1]
+    assert K % 32 == 0
+    codes = np.empty(v.shape, np.uint8)
+    scales = np.empty(v.shape[:-1] + (K // 32,), np.uint8)
+    _load().syn_quant_mxfp8(v.ctypes.data, v.size, codes.ctypes.data, scales.ctypes.data, _nth())
+    return codes, scales
 
 
 def topk_routing(T: int, E: int, topk: int, seed: int):
