@@ -189,9 +189,8 @@ _WS_CACHE = {}
 
 
 def workspace(nbytes: int, key=None) -> Optional[torch.Tensor]:
-    """A zero-filled device workspace of at least nbytes, cached per device and
-    key.  Split-K counters inside it are left at zero by every call, so one
-    workspace serves every later call issued on the same stream."""
+    """A device workspace of at least nbytes, cached per device and key (grown
+    on demand).  Calls that share one must be ordered on one stream."""
     if nbytes == 0:
         return None
     dev = torch.cuda.current_device()

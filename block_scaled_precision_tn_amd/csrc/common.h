@@ -83,6 +83,16 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
   return (b & 0x80u) ? -v : v;
 }
 
+// E4M3-FN byte -> FP32 value x 64, in three integer/float operations: the
+// byte's exponent and mantissa fields placed in an FP32 pattern give
+// 2^(e-127)(1+m/8) for e >= 1 and, as an FP32 subnormal, m * 2^-129 for
+// e == 0; one multiply by 2^126 rescales both cases to 64 * value exactly.
+// (NaN bytes are not special-cased.)
+__device__ __forceinline__ float e4m3_x64_to_f32(uint32_t b) {
+  const float f = __builtin_bit_cast(float, ((b & 0x7Fu) << 20) | ((b & 0x80u) << 24));
+  return f * 8.5070591730234616e+37f;  // 2^126
+}
+
 // FP32 -> BF16 bits, round to nearest even (NaN stays NaN)
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   uint32_t u = __builtin_bit_cast(uint32_t, f);

@@ -8,189 +8,303 @@
 //   * acc = fma(64 * s_w[n,g], P_g, acc) in FP32 (the folded 2^6);
 //   * epilogue: acc * a_tok[m] * S_w.
 //
-// The operation is bound by the weight stream (N*K/2 code bytes + N*K/16
-// scale bytes), so every CU must stream its share of W at full rate.  Work
-// split: a workgroup owns 32 weight rows (the MFMA's B side: one lane column
-// per weight row, so the per-row group scale is one value per lane) and a
-// contiguous K range; its 4 waves take interleaved 32-element group pairs of
-// that range and are reduced through LDS in wave order.  K ranges are split
-// over `ks` workgroups (split-K); their FP32 partials go to the workspace and
-// the last-arriving workgroup of each weight tile sums them in split order
-// 0..ks-1, so the result is bit-identical run to run.  The tokens sit on the
-// MFMA's A side (rows), padded to 32 per block; for M <= 32 only the
-// accumulator registers that hold real tokens are scaled.
+// The operation streams the weight (N*K/2 code bytes + N*K/16 scale bytes)
+// once per 32 tokens, so it is arranged for HBM:
+//   * HBM reads run fastest when a wave reads long contiguous runs of one
+//     weight row, while the MFMA's B operand wants one weight row per lane.
+//     A workgroup therefore loads its 128 weight rows x 512 K-elements
+//     coalesced (16 lanes cover the 256-byte code run of one row), with the
+//     rows' scale bytes and the token rows, into LDS; each wave then computes
+//     its 32-row slab from LDS.  Code rows are XOR-swizzled in 16-byte chunks
+//     so the 32 rows one operand read touches spread over the LDS banks;
+//     token rows are padded by 8 bytes for the same reason.
+//   * each workgroup covers two consecutive 512-element ranges; the loads of
+//     both are issued together, so the second range arrives (in registers)
+//     while the first is computed from LDS.
+//   * the K ranges of a weight tile are split over ks workgroups (split-K);
+//     each writes an FP32 partial, and a second kernel sums the partials in
+//     split order 0..ks-1 -- results are bit-identical run to run.
+// Tokens sit on the MFMA's A side, padded to 32: lanes of token rows >= M
+// read row 0 (those MFMA rows are never stored), and only the accumulator
+// registers that hold real tokens are scaled.  M > 32 runs in slices of 32.
 #include "common.h"
 #include "kernels.h"
 
 namespace mg {
 namespace {
 
-constexpr int NT = 32;        // weight rows per workgroup
-constexpr int MAXM = 128;     // tokens per launch (larger M runs in slices)
+constexpr int NT = 128;       // weight rows per workgroup (4 waves x 32)
+constexpr int KR = 512;       // K-elements per range
+constexpr int RPW = 2;        // ranges per workgroup
+static_assert(RPW == 2, "the decode kernel holds exactly two ranges in flight");
+constexpr int MS = 32;        // tokens per launch
 
-int choose_ks(int M, int N, int K) {
-  const int ntiles = (N + NT - 1) / NT;
-  const int pairs = K / 32;
-  const int target = M <= 32 ? 768 : 384;   // workgroups wanted in flight
-  int ks = (target + ntiles - 1) / ntiles;
-  ks = ks < 1 ? 1 : ks;
-  ks = ks > 16 ? 16 : ks;
-  while (ks > 1 && pairs / ks < 8) --ks;    // keep >= 2 pairs per wave
-  return ks;
+constexpr int ROWB = KR / 2;          // code bytes per weight row per range
+constexpr int CHUNKS = ROWB / 16;     // 16-byte chunks per code row (2 groups each)
+constexpr int SB = KR / 16;           // scale bytes per row per range
+constexpr int SROW = SB + 4;          // LDS bytes per scale row (padded)
+constexpr int AROW = KR + 16;         // LDS bytes per token row (padded)
+
+// MT token rows (8 per accumulator quad in use): 41600 bytes at MT = 8,
+// 54272 at MT = 32
+template <int MT>
+struct Tile {
+  uint8_t w[NT * ROWB];
+  uint8_t s[NT * SROW];
+  uint8_t a[MT * AROW];
+};
+
+constexpr int WCH = NT * CHUNKS / 256;          // code chunks per thread
+constexpr int SCH = NT * SB / 16 / 256 > 0 ? NT * SB / 16 / 256 : 1;
+
+// Code chunk c of weight row `row` (K-elements 32c .. 32c+31) sits at
+// woff(row, c) with its four dwords reordered [d0 d2 d1 d3], where d0/d1 are
+// the low/high halves of group 2c and d2/d3 those of group 2c+1: the lane
+// that feeds MFMA K-half h then reads both groups' slices as one 8-byte word.
+__device__ __forceinline__ int woff(int row, int chunk) {
+  return row * ROWB + ((chunk ^ (row & (CHUNKS - 1))) << 4);
 }
 
-template <int MB, int QUADS>
-__global__ __launch_bounds__(256) void w4a8_decode_kernel(W4A8Args p, int ks, float *part,
-                                                          uint32_t *cnt) {
-  __shared__ float red[4][MB * 16][64];
-  __shared__ int s_last;
+template <int MT>
+struct RangeRegs {
+  static constexpr int ACH = MT * (KR / 16) / 256;  // token chunks per thread
+  u32x4 w[WCH];
+  u32x4 s[SCH];
+  u32x4 a[ACH];
+};
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
-  const int nt = blockIdx.x, kc = blockIdx.y;
-  const int n = nt * NT + l32;
-  const int nrow = n < p.N ? n : p.N - 1;
-  const int P = p.K / 32;
-  const int pbeg = (int)((int64_t)kc * P / ks), pend = (int)((int64_t)(kc + 1) * P / ks);
-
-  f32x16 acc[MB];
+// loads of K range [k0, k0 + klen) of this workgroup's weight tile and tokens
+template <int MT>
+__device__ __forceinline__ void range_load(const W4A8Args &p, int n0, int k0, int klen, int tid,
+                                           RangeRegs<MT> &r) {
+  constexpr int ACH = RangeRegs<MT>::ACH;
+  const int G = p.K / 16;
 #pragma unroll
-  for (int b = 0; b < MB; ++b) acc[b] = f32x16{0};
-  const f32x16 zero = {0};
-
-  const uint8_t *wrow = p.wq + (int64_t)nrow * (p.K / 2);
-  const uint8_t *srow = p.ws + (int64_t)nrow * (p.K / 16);
-
-
-  for (int pp = pbeg + wave; pp < pend; pp += 4) {
-    const u32x4 wc = *(const u32x4 *)(wrow + (int64_t)pp * 16);
-    const uint32_t sb = *(const uint16_t *)(srow + (int64_t)pp * 2);
-    uint64_t fa[2][MB];
+  for (int i = 0; i < WCH; ++i) {
+    const int c = tid + 256 * i, row = c / CHUNKS, ch = c % CHUNKS;
+    const int n = n0 + row < p.N ? n0 + row : p.N - 1;
+    const bool in = ch * 32 < klen;
+    const u32x4 v = *(const u32x4 *)(p.wq + (int64_t)n * (p.K / 2) + k0 / 2 + (in ? ch : 0) * 16);
+    r.w[i] = in ? v : u32x4{0, 0, 0, 0};
+  }
 #pragma unroll
-    for (int gi = 0; gi < 2; ++gi)
-#pragma unroll
-      for (int b = 0; b < MB; ++b) {
-        const int t = b * 32 + l32;
-        fa[gi][b] = t < p.M ? *(const uint64_t *)(p.aq + (int64_t)t * p.K + (2 * pp + gi) * 16 + 8 * h)
-                            : (uint64_t)0;
+  for (int i = 0; i < SCH; ++i) {
+    const int c = tid + 256 * i, row = c / (SB / 16), ch = c % (SB / 16);
+    const int n = n0 + row < p.N ? n0 + row : p.N - 1;
+    const bool in = row < NT && ch * 256 < klen;
+    u32x4 v = {0, 0, 0, 0};
+    if ((G % 16) == 0) {
+      const u32x4 x = *(const u32x4 *)(p.ws + (int64_t)n * G + k0 / 16 + (in ? ch : 0) * 16);
+      v = in ? x : v;
+    } else if (in) {
+      uint32_t b[4] = {0, 0, 0, 0};
+      for (int e = 0; e < 16; ++e) {
+        const int g = k0 / 16 + ch * 16 + e;
+        if (g < G) b[e >> 2] |= (uint32_t)p.ws[(int64_t)n * G + g] << (8 * (e & 3));
       }
+      v = u32x4{b[0], b[1], b[2], b[3]};
+    }
+    r.s[i] = v;
+  }
 #pragma unroll
-    for (int gi = 0; gi < 2; ++gi) {
-      const uint64_t fw = nvfp4x8_to_e4m3x8(wc[2 * gi + h]);
-      const float s64 = e4m3_to_f32((sb >> (8 * gi)) & 0xFFu) * 64.0f;
+  for (int i = 0; i < ACH; ++i) {
+    const int c = tid + 256 * i, t = c / (KR / 16), ch = c % (KR / 16);
+    const bool in = t < p.M && ch * 16 < klen;
+    const int tt = t < p.M ? t : p.M - 1;
+    const u32x4 x = *(const u32x4 *)(p.aq + (int64_t)tt * p.K + k0 + (in ? ch : 0) * 16);
+    r.a[i] = in ? x : u32x4{0, 0, 0, 0};
+  }
+}
+
+template <int MT>
+__device__ __forceinline__ void range_store(Tile<MT> &tile, int M, int tid, const RangeRegs<MT> &r) {
+  constexpr int ACH = RangeRegs<MT>::ACH;
 #pragma unroll
-      for (int b = 0; b < MB; ++b) {
-        const f32x16 pg = mfma_fp8(e4m3x8_even_odd(fa[gi][b]), fw, zero);
+  for (int i = 0; i < WCH; ++i) {
+    const int c = tid + 256 * i, row = c / CHUNKS, ch = c % CHUNKS;
+    const u32x4 v = r.w[i];
+    *(u32x4 *)(tile.w + woff(row, ch)) = u32x4{v[0], v[2], v[1], v[3]};
+  }
 #pragma unroll
-        for (int r = 0; r < 4 * QUADS; ++r) acc[b][r] = __builtin_fmaf(s64, pg[r], acc[b][r]);
-      }
+  for (int i = 0; i < SCH; ++i) {
+    const int c = tid + 256 * i, row = c / (SB / 16), ch = c % (SB / 16);
+    if (c < NT * SB / 16) {
+      uint32_t *dst = (uint32_t *)(tile.s + row * SROW + ch * 16);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dst[j] = r.s[i][j];
     }
   }
+#pragma unroll
+  for (int i = 0; i < ACH; ++i) {
+    const int c = tid + 256 * i, t = c / (KR / 16), g = c % (KR / 16);
+    if (t < M) {
+      // each 8-byte slice in even/odd byte order (the converted weight codes
+      // come out in that order); the slices of groups 2c and 2c+1 that one
+      // MFMA K-half reads are placed side by side: [lo(2c) lo(2c+1) | hi(2c) hi(2c+1)]
+      const uint64_t lo = e4m3x8_even_odd((uint64_t)r.a[i][0] | ((uint64_t)r.a[i][1] << 32));
+      const uint64_t hi = e4m3x8_even_odd((uint64_t)r.a[i][2] | ((uint64_t)r.a[i][3] << 32));
+      uint8_t *dst = tile.a + t * AROW + 32 * (g >> 1) + 8 * (g & 1);
+      *(uint64_t *)dst = lo;
+      *(uint64_t *)(dst + 16) = hi;
+    }
+  }
+}
 
-  // reduce the 4 waves in wave order
+// np pairs of 16-element groups (2 groups per code chunk) from the LDS tile
+template <int QUADS, bool FULL>
+__device__ __forceinline__ void compute_range(const Tile<8 * QUADS> &tile, int row, int trow, int h, int np,
+                                              f32x16 &acc) {
+  const uint8_t *wrow = tile.w + row * ROWB + 8 * h;
+  const uint8_t *arow = tile.a + trow * AROW + 16 * h;
+  const uint8_t *srow = tile.s + row * SROW;
+  const f32x16 zero = {0};
+  auto pair = [&](int c) {
+    const uint64_t cw = *(const uint64_t *)(wrow + ((c ^ (row & (CHUNKS - 1))) << 4));
+    const u32x4 av = *(const u32x4 *)(arow + 32 * c);
+    const uint32_t sc = *(const uint16_t *)(srow + 2 * c);
+    const float s0 = e4m3_x64_to_f32(sc & 0xFFu), s1 = e4m3_x64_to_f32(sc >> 8);
+    const uint64_t a0 = (uint64_t)av[0] | ((uint64_t)av[1] << 32);
+    const uint64_t a1 = (uint64_t)av[2] | ((uint64_t)av[3] << 32);
+    const f32x16 p0 = mfma_fp8(a0, nvfp4x8_to_e4m3x8((uint32_t)cw), zero);
+    const f32x16 p1 = mfma_fp8(a1, nvfp4x8_to_e4m3x8((uint32_t)(cw >> 32)), zero);
 #pragma unroll
-  for (int b = 0; b < MB; ++b)
+    for (int r = 0; r < 4 * QUADS; ++r) acc[r] = __builtin_fmaf(s0, p0[r], acc[r]);
 #pragma unroll
-    for (int r = 0; r < 4 * QUADS; ++r) red[wave][b * 16 + r][lane] = acc[b][r];
+    for (int r = 0; r < 4 * QUADS; ++r) acc[r] = __builtin_fmaf(s1, p1[r], acc[r]);
+  };
+  if constexpr (FULL) {
+#pragma unroll
+    for (int c = 0; c < CHUNKS; ++c) pair(c);
+  } else {
+    for (int c = 0; c < np; ++c) pair(c);
+  }
+}
+
+template <int QUADS>
+__device__ __forceinline__ void compute_any(const Tile<8 * QUADS> &tile, int row, int trow, int h, int klen,
+                                            f32x16 &acc) {
+  if (klen == KR)
+    compute_range<QUADS, true>(tile, row, trow, h, CHUNKS, acc);
+  else
+    compute_range<QUADS, false>(tile, row, trow, h, klen / 32, acc);
+}
+
+template <int QUADS>
+__global__ __launch_bounds__(256) void w4a8_decode_kernel(W4A8Args p, int ks, float *part) {
+  __shared__ __attribute__((aligned(16))) Tile<8 * QUADS> tile;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int nt = blockIdx.x, kc = blockIdx.y;
+  const int n0 = nt * NT;
+  const int nrange = (p.K + KR - 1) / KR;
+  const int rbeg = kc * RPW;
+  const bool two = rbeg + 1 < nrange;  // RPW == 2
+
+  const int row = wave * 32 + l32;
+  const int trow = l32 < p.M ? l32 : 0;
+  f32x16 acc = {0};
+
+  // both ranges' loads go out at once; the second lands while the first computes
+  const int k0a = rbeg * KR, klena = p.K - k0a < KR ? p.K - k0a : KR;
+  const int k0b = two ? k0a + KR : k0a, klenb = p.K - k0b < KR ? p.K - k0b : KR;
+  RangeRegs<8 * QUADS> ra, rb;
+  range_load(p, n0, k0a, klena, tid, ra);
+  range_load(p, n0, k0b, klenb, tid, rb);
+  range_store(tile, p.M, tid, ra);
   __syncthreads();
+  compute_any<QUADS>(tile, row, trow, h, klena, acc);
+  if (two) {
+    __syncthreads();
+    range_store(tile, p.M, tid, rb);
+    __syncthreads();
+    compute_any<QUADS>(tile, row, trow, h, klenb, acc);
+  }
 
-  const float sw = *p.Sw;
+  const int n = n0 + row;
+  if (n >= p.N) return;
   if (ks == 1) {
-    if (wave == 0 && n < p.N) {
+    const float sw = *p.Sw;
 #pragma unroll
-      for (int b = 0; b < MB; ++b)
-#pragma unroll
-        for (int r = 0; r < 4 * QUADS; ++r) {
-          const int t = b * 32 + acc_row(r, lane);
-          if (t >= p.M) continue;
-          const int q = b * 16 + r;
-          const float v = (((red[0][q][lane] + red[1][q][lane]) + red[2][q][lane]) + red[3][q][lane]) *
-                          (p.atok[t] * sw);
-          if (p.out_f32)
-            ((float *)p.C)[(int64_t)t * p.N + n] = v;
-          else
-            ((uint16_t *)p.C)[(int64_t)t * p.N + n] = (uint16_t)f32_to_bf16_rne(v);
-        }
+    for (int r = 0; r < 4 * QUADS; ++r) {
+      const int t = acc_row(r, lane);
+      if (t >= p.M) continue;
+      const float v = acc[r] * (p.atok[t] * sw);
+      if (p.out_f32)
+        ((float *)p.C)[(int64_t)t * p.N + n] = v;
+      else
+        ((uint16_t *)p.C)[(int64_t)t * p.N + n] = (uint16_t)f32_to_bf16_rne(v);
     }
     return;
   }
-
-  // split-K: publish this split's partial, the last arrival reduces in order
-  if (wave == 0 && n < p.N) {
 #pragma unroll
-    for (int b = 0; b < MB; ++b)
-#pragma unroll
-      for (int r = 0; r < 4 * QUADS; ++r) {
-        const int t = b * 32 + acc_row(r, lane);
-        if (t >= p.M) continue;
-        const int q = b * 16 + r;
-        part[((int64_t)kc * p.M + t) * p.N + n] =
-            ((red[0][q][lane] + red[1][q][lane]) + red[2][q][lane]) + red[3][q][lane];
-      }
+  for (int r = 0; r < 4 * QUADS; ++r) {
+    const int t = acc_row(r, lane);
+    if (t < p.M) part[((int64_t)kc * p.M + t) * p.N + n] = acc[r];
   }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) s_last = atomicAdd(&cnt[nt], 1u) == (uint32_t)(ks - 1);
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  for (int e = tid; e < p.M * NT; e += 256) {
-    const int t = e / NT, nn = nt * NT + (e % NT);
-    if (nn >= p.N) continue;
-    float v = 0.0f;
-    for (int s = 0; s < ks; ++s) v += part[((int64_t)s * p.M + t) * p.N + nn];
-    v *= p.atok[t] * sw;
-    if (p.out_f32)
-      ((float *)p.C)[(int64_t)t * p.N + nn] = v;
-    else
-      ((uint16_t *)p.C)[(int64_t)t * p.N + nn] = (uint16_t)f32_to_bf16_rne(v);
-  }
-  if (tid == 0) atomicExch(&cnt[nt], 0u);  // leave the counter ready for the next call
 }
 
-template <int MB, int QUADS>
-void launch_one(const W4A8Args &p, int ks, float *part, uint32_t *cnt, hipStream_t stream) {
+// C[t,n] = (sum over splits s = 0..ks-1, in order, of part[s,t,n]) * a_tok[t] * S_w
+__global__ __launch_bounds__(64) void w4a8_splitk_reduce(W4A8Args p, int ks, const float *part) {
+  const int64_t i = (int64_t)blockIdx.x * 64 + threadIdx.x;
+  const int64_t mn = (int64_t)p.M * p.N;
+  if (i >= mn) return;
+  const int t = (int)(i / p.N);
+  float v = 0.0f;
+  int s = 0;
+  for (; s + 8 <= ks; s += 8) {  // eight independent loads in flight, summed in order
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = part[(int64_t)(s + j) * mn + i];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v += x[j];
+  }
+  for (; s < ks; ++s) v += part[(int64_t)s * mn + i];
+  v *= p.atok[t] * *p.Sw;
+  if (p.out_f32)
+    ((float *)p.C)[i] = v;
+  else
+    ((uint16_t *)p.C)[i] = (uint16_t)f32_to_bf16_rne(v);
+}
+
+int splits(int K) {
+  const int nrange = (K + KR - 1) / KR;
+  return (nrange + RPW - 1) / RPW;
+}
+
+template <int QUADS>
+void launch_one(const W4A8Args &p, int ks, float *part, hipStream_t stream) {
   dim3 grid((p.N + NT - 1) / NT, ks);
-  hipLaunchKernelGGL((w4a8_decode_kernel<MB, QUADS>), grid, dim3(256), 0, stream, p, ks, part, cnt);
+  hipLaunchKernelGGL((w4a8_decode_kernel<QUADS>), grid, dim3(256), 0, stream, p, ks, part);
 }
-
-// Workspace: a fixed 64 KiB counter region first (one counter per 32-row
-// weight tile; left at zero by every call), then the split partials.  The
-// fixed placement keeps the counters away from partials of any earlier call.
-constexpr size_t kCounterBytes = 65536;
 
 }  // namespace
 
 size_t w4a8_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  const int64_t Ms = M < MAXM ? M : MAXM;
-  const int ks = choose_ks((int)Ms, (int)N, (int)K);
+  const int ks = splits((int)K);
   if (ks <= 1) return 0;
-  return kCounterBytes + (size_t)ks * (size_t)Ms * (size_t)N * sizeof(float);
+  const int64_t Ms = M < MS ? M : MS;
+  return (size_t)ks * (size_t)Ms * (size_t)N * sizeof(float);
 }
 
-int64_t w4a8_max_n() { return (int64_t)(kCounterBytes / sizeof(uint32_t)) * NT; }
+int64_t w4a8_max_n() { return (int64_t)1 << 30; }
 
 hipError_t launch_w4a8(const W4A8Args &p0, hipStream_t stream) {
-  for (int m0 = 0; m0 < p0.M; m0 += MAXM) {
+  const int ks = splits(p0.K);
+  for (int m0 = 0; m0 < p0.M; m0 += MS) {
     W4A8Args p = p0;
-    p.M = p0.M - m0 < MAXM ? p0.M - m0 : MAXM;
+    p.M = p0.M - m0 < MS ? p0.M - m0 : MS;
     p.aq = p0.aq + (int64_t)m0 * p0.K;
     p.atok = p0.atok + m0;
     p.C = (char *)p0.C + (int64_t)m0 * p0.N * (p0.out_f32 ? 4 : 2);
-    const int Mslice = p0.M < MAXM ? p0.M : MAXM;
-    const int ks = choose_ks(Mslice, p.N, p.K);
-    float *part = nullptr;
-    uint32_t *cnt = nullptr;
+    float *part = ks > 1 ? (float *)p0.work : nullptr;
+    if (p.M > 24) launch_one<4>(p, ks, part, stream);
+    else if (p.M > 16) launch_one<3>(p, ks, part, stream);
+    else if (p.M > 8) launch_one<2>(p, ks, part, stream);
+    else launch_one<1>(p, ks, part, stream);
     if (ks > 1) {
-      cnt = (uint32_t *)p0.work;
-      part = (float *)((char *)p0.work + kCounterBytes);
+      const int64_t mn = (int64_t)p.M * p.N;
+      hipLaunchKernelGGL(w4a8_splitk_reduce, dim3((unsigned)((mn + 63) / 64)), dim3(64), 0,
+                         stream, p, ks, part);
     }
-    if (p.M > 96) launch_one<4, 4>(p, ks, part, cnt, stream);
-    else if (p.M > 64) launch_one<3, 4>(p, ks, part, cnt, stream);
-    else if (p.M > 32) launch_one<2, 4>(p, ks, part, cnt, stream);
-    else if (p.M > 24) launch_one<1, 4>(p, ks, part, cnt, stream);
-    else if (p.M > 16) launch_one<1, 3>(p, ks, part, cnt, stream);
-    else if (p.M > 8) launch_one<1, 2>(p, ks, part, cnt, stream);
-    else launch_one<1, 1>(p, ks, part, cnt, stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

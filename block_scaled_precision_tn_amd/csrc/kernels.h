@@ -39,10 +39,10 @@ struct W4A8Args {
   void *C;
   int M, N, K;
   int out_f32;
-  void *work;       // split-K partials then per-tile arrival counters (launcher's layout)
+  void *work;       // split-K partials [splits, M, N] FP32
 };
 size_t w4a8_workspace_bytes(int64_t M, int64_t N, int64_t K);
-int64_t w4a8_max_n();  // largest N the counter region supports
+int64_t w4a8_max_n();  // largest N the decode kernel's indexing supports
 hipError_t launch_w4a8(const W4A8Args &p, hipStream_t stream);
 
 struct MoeArgs {

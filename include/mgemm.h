@@ -142,14 +142,12 @@ int mgemm_w4a16(const void *A, const void *Wq, const void *Ws, const float *Sw,
    weight codes converted by the E2M1 -> E4M3 bit identity, one FP8 MFMA per
    16-element group, the group scale (times 64) applied in FP32 per group,
    a_tok[m] * Sw in the epilogue.  The decode kernel splits K over
-   workgroups and needs a workspace: `ws` device memory of at least
-   mgemm_workspace_bytes(MGEMM_OP_W4A8, M, N, K, ...) bytes (when that is 0,
-   ws may be NULL).  The workspace must be zero-filled before its first use;
-   every call leaves its arrival counters at zero again, so one workspace
-   serves any later call of the same or smaller size.  Calls that share a
-   workspace must be ordered on one stream.  Split partials are reduced in a
-   fixed order: results are run-to-run bit-identical.  M is processed in
-   slices of 128 rows; N may be at most 524288. */
+   workgroups: each writes FP32 partial sums to `ws`, and a second kernel
+   adds them in split order (results are run-to-run bit-identical).  `ws` is
+   device memory of at least mgemm_workspace_bytes(MGEMM_OP_W4A8, M, N, K,
+   ...) bytes, 16-byte aligned, with no required contents (when the size is
+   0, ws may be NULL).  Calls that share a workspace must be ordered on one
+   stream.  M is processed in slices of 32 rows. */
 int mgemm_w4a8(const void *Aq, const float *a_tok, const void *Wq, const void *Ws,
                const float *Sw, void *C, int64_t M, int64_t N, int64_t K, int out_f32,
                void *ws, size_t ws_bytes, void *stream);

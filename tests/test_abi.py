@@ -117,7 +117,7 @@ def test_host_side_argument_errors(lib):
     assert lib.mgemm_w4a16(p, p, p, p, p, 32, 32, 16, 0, None) == -2
     assert lib.mgemm_w4a8(p, p, p, p, p, p, 8, 32, 0, 0, p, 0, None) == -2
     assert lib.mgemm_w4a8(p, None, p, p, p, p, 8, 32, 32, 0, p, 0, None) == -1
-    assert lib.mgemm_w4a8(p, p, p, p, p, p, 8, 600000, 14336, 0, p, 1 << 30, None) == -2
+    assert lib.mgemm_w4a8(p, p, p, p, p, p, 8, (1 << 30) + 128, 14336, 0, p, 1 << 40, None) == -2
     moe = lambda **kw: lib.mgemm_moe_mxfp8_glu(  # noqa: E731
         p, p, p, p, kw.get("T", 64), kw.get("H", 128), kw.get("I", 128), kw.get("E", 4),
         kw.get("topk", 2), p, p, p, p, p, p, 1 << 30, None, None)

@@ -148,7 +148,9 @@ def test_w4a16_parity(M, N, K):
 
 
 @pytest.mark.parametrize("M", [1, 3, 8, 17, 32, 33, 100, 128, 200])
-@pytest.mark.parametrize("N,K", [(96, 256), (200, 1024), (384, 2048)])
+@pytest.mark.parametrize("N,K", [(96, 256), (200, 1024), (384, 2048),
+                                 (130, 1536),    # odd number of 512-element K ranges
+                                 (257, 1568)])   # partial last range, K/16 not a multiple of 16
 def test_w4a8_parity(M, N, K):
     from gpu_cases import check_both, oracle_full
     inp = synth.w4a8(M, N, K, seed=M + N)
@@ -157,8 +159,8 @@ def test_w4a8_parity(M, N, K):
 
 
 def test_w4a8_workspace_reuse_across_sizes():
-    """One workspace serves a large call then a smaller one (counters are left
-    at zero by every call)."""
+    """One workspace serves a large call then smaller ones (the split-K
+    partials it holds need no clearing between calls)."""
     from gpu_cases import check_both, oracle_full
     for M, N, K in [(128, 384, 2048), (8, 200, 1024), (32, 384, 2048), (1, 96, 256)]:
         inp = synth.w4a8(M, N, K, seed=7 * M + 1)
