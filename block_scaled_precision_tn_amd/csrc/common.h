@@ -15,6 +15,7 @@
 #include <stdint.h>
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x32 __attribute__((ext_vector_type(32)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -91,6 +92,20 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
 __device__ __forceinline__ float e4m3_x64_to_f32(uint32_t b) {
   const float f = __builtin_bit_cast(float, ((b & 0x7Fu) << 20) | ((b & 0x80u) << 24));
   return f * 8.5070591730234616e+37f;  // 2^126
+}
+
+// The same with the E4M3 NaN bytes (0x7F, 0xFF) mapped to a NaN.
+__device__ __forceinline__ float e4m3_x64_to_f32_nan(uint32_t b) {
+  const float v = e4m3_x64_to_f32(b);
+  return (b & 0x7Fu) == 0x7Fu ? __builtin_nanf("") : v;
+}
+
+// Two 32x32 outer products of K = 1 in FP32 (v_mfma_f32_32x32x1_2b_f32):
+// output registers 16b..16b+15 hold block b, laid out as any 32x32 MFMA
+// result, with block b's (row i, column j) = a[lane 32b+i] * b[lane 32b+j].
+__device__ __forceinline__ f32x32 mfma_outer2(float a, float b) {
+  const f32x32 z = {0};
+  return __builtin_amdgcn_mfma_f32_32x32x1f32(a, b, z, 0, 0, 0);
 }
 
 // FP32 -> BF16 bits, round to nearest even (NaN stays NaN)
