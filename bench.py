@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--only", default="", help="w4a4|w4a8|bf16|moe (profiling runs)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run one plain copy kernel of this many MiB (counter calibration)")
+    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU work: turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
+                         "'--only w4a4 --copy-calib-mib N' into profiles/traffic.json")
     return ap.parse_args()
 
 
@@ -70,6 +73,53 @@ def traffic_for(kernel_file, key):
     return d.get("bytes_per_launch")
 
 
+def _pmc_means(d, counter):
+    """Mean counter value per dispatch, by kernel name, from a rocprofv3 --pmc
+    CSV directory."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    acc = {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] != counter:
+                continue
+            acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def write_traffic(fetch_dir, write_dir, calib_mib):
+    """HBM traffic of the W4A4 kernel per launch: FETCH_SIZE and WRITE_SIZE (KiB
+    per dispatch), each scaled by bytes/KiB-read of the plain copy kernel of
+    known size from the same run (it reads and writes calib_mib MiB)."""
+    fetch, write = _pmc_means(fetch_dir, "FETCH_SIZE"), _pmc_means(write_dir, "WRITE_SIZE")
+    pick = lambda d, sub: [v for k, v in d.items() if sub in k]  # noqa: E731
+    kf, kw = pick(fetch, "w4a4_fp8route_kernel"), pick(write, "w4a4_fp8route_kernel")
+    cf, cw = pick(fetch, "MulFunctor"), pick(write, "MulFunctor")
+    if not (kf and kw and cf and cw):
+        raise SystemExit(f"kernels not found: {sorted(fetch)}")
+    nbytes = calib_mib * (1 << 20)
+    f_fetch, f_write = nbytes / (cf[0] * 1024), nbytes / (cw[0] * 1024)
+    t_fetch, t_write = kf[0] * 1024 * f_fetch, kw[0] * 1024 * f_write
+    algo = M * K // 2 + M * K // 16 + N * K // 2 + N * K // 16 + 8 + 2 * M * N
+    out = {"w4a4_m8192": {
+        "src_hash": src_hash("gemm_w4a4.hip", "common.h"),
+        "bytes_per_launch": round(t_fetch + t_write),
+        "fetch_bytes": round(t_fetch), "write_bytes": round(t_write),
+        "fetch_kib_raw": kf[0], "write_kib_raw": kw[0],
+        "copy_calibration": {"mib": calib_mib, "fetch_kib_raw": cf[0], "write_kib_raw": cw[0],
+                             "fetch_factor": f_fetch, "write_factor": f_write},
+        "algorithmic_bytes": algo,
+        "traffic_over_algorithmic": round((t_fetch + t_write) / algo, 3)}}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
 def timed(torch, fn, steps, warmup, stream):
     for _ in range(warmup):
         fn(0)
@@ -86,6 +136,9 @@ def timed(torch, fn, steps, warmup, stream):
 
 def main():
     args = parse()
+    if args.traffic:
+        write_traffic(args.traffic[0], args.traffic[1], args.copy_calib_mib or 1024)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
               "this library has no multi-GPU path", file=sys.stderr)

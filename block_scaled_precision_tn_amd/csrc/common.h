@@ -119,6 +119,23 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
 }
 
+// Tile of a 1-D launch of T = tiles_m * tiles_n workgroups, chosen for L2 reuse
+// on a chip whose XCDs (each with its own L2) receive workgroups round-robin
+// (workgroup id i runs on XCD i % 8): each XCD gets one contiguous run of the
+// tile order, and that order walks groups of 8 tile rows column by column, so
+// the workgroups running together on an XCD share A row panels and W column
+// panels.
+__device__ __forceinline__ void xcd_tile(int id, int tiles_m, int tiles_n, int &tm, int &tn) {
+  constexpr int XCDS = 8, GROUP = 8;
+  const int T = tiles_m * tiles_n, q = T / XCDS, r = T % XCDS;
+  const int x = id % XCDS, j = id / XCDS;
+  const int t = x < r ? x * (q + 1) + j : r * (q + 1) + (x - r) * q + j;
+  const int per_group = GROUP * tiles_n, first = (t / per_group) * GROUP;
+  const int gsz = tiles_m - first < GROUP ? tiles_m - first : GROUP;
+  tm = first + (t % per_group) % gsz;
+  tn = (t % per_group) / gsz;
+}
+
 // row held by accumulator register r of lane l (see the layout note above)
 __device__ __forceinline__ int acc_row(int r, int lane) {
   return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);

@@ -107,7 +107,9 @@ __global__ __launch_bounds__(512, 2) void w4a4_fp8route_kernel(W4A4Args p) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, h = lane >> 5;
-  const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
+  int tm, tn;
+  xcd_tile(blockIdx.x, (p.M + BM - 1) / BM, (p.N + BN - 1) / BN, tm, tn);
+  const int n0 = tn * BN, m0 = tm * BM;
   const int G = p.K / 16;
   const int S = (G + GPS - 1) / GPS;
 
@@ -176,7 +178,7 @@ __global__ __launch_bounds__(512, 2) void w4a4_fp8route_kernel(W4A4Args p) {
 }  // namespace
 
 hipError_t launch_w4a4(const W4A4Args &p, hipStream_t stream) {
-  dim3 grid((p.N + BN - 1) / BN, (p.M + BM - 1) / BM);
+  dim3 grid(((p.N + BN - 1) / BN) * ((p.M + BM - 1) / BM));
   hipLaunchKernelGGL(w4a4_fp8route_kernel, grid, dim3(512), 0, stream, p);
   return hipGetLastError();
 }
