@@ -12,15 +12,16 @@
 // once per 32 tokens, so it is arranged for HBM:
 //   * HBM reads run fastest when a wave reads long contiguous runs of one
 //     weight row, while the MFMA's B operand wants one weight row per lane.
-//     A workgroup therefore loads its 128 weight rows x 512 K-elements
-//     coalesced (16 lanes cover the 256-byte code run of one row), with the
+//     A workgroup therefore loads its 128 weight rows x 256 K-elements
+//     coalesced (8 lanes cover the 128-byte code run of one row), with the
 //     rows' scale bytes and the token rows, into LDS; each wave then computes
 //     its 32-row slab from LDS.  Code rows are XOR-swizzled in 16-byte chunks
 //     so the 32 rows one operand read touches spread over the LDS banks;
 //     token rows are padded by 8 bytes for the same reason.
-//   * each workgroup covers two consecutive 512-element ranges; the loads of
-//     both are issued together, so the second range arrives (in registers)
-//     while the first is computed from LDS.
+//   * K is cut into 256-element ranges, four per workgroup; all four are
+//     requested at once (register buffers), so the whole weight stream is in
+//     flight from the start, and each range is staged and computed as it
+//     lands -- the work left after the last bytes arrive is one short range.
 //   * the K ranges of a weight tile are split over ks workgroups (split-K);
 //     each writes an FP32 partial, and a second kernel sums the partials in
 //     split order 0..ks-1 -- results are bit-identical run to run.
@@ -34,47 +35,46 @@ namespace mg {
 namespace {
 
 constexpr int NT = 128;       // weight rows per workgroup (4 waves x 32)
-constexpr int KR = 512;       // K-elements per range
-constexpr int RPW = 2;        // ranges per workgroup
-static_assert(RPW == 2, "the decode kernel holds exactly two ranges in flight");
+constexpr int KR = 256;       // K-elements per range
+constexpr int RPW = 4;        // ranges per workgroup, all requested at once
 constexpr int MS = 32;        // tokens per launch
 
 constexpr int ROWB = KR / 2;          // code bytes per weight row per range
 constexpr int CHUNKS = ROWB / 16;     // 16-byte chunks per code row (2 groups each)
 constexpr int SB = KR / 16;           // scale bytes per row per range
-constexpr int SROW = SB + 4;          // LDS bytes per scale row (padded)
+constexpr int SROWF = SB + 2;         // LDS floats per scale row (padded: rows hit distinct banks)
 constexpr int AROW = KR + 16;         // LDS bytes per token row (padded)
 
-// MT token rows (8 per accumulator quad in use): 41600 bytes at MT = 8,
-// 54272 at MT = 32
+// MT token rows (8 per accumulator quad in use): 20992 bytes at MT = 8,
+// 27520 at MT = 32
 template <int MT>
 struct Tile {
+  static constexpr int AROWS = (MT * (KR / 16) + 255) / 256 * 256 / (KR / 16);  // rows the loads cover
   uint8_t w[NT * ROWB];
-  uint8_t s[NT * SROW];
-  uint8_t a[MT * AROW];
+  float s[NT * SROWF];      // group scales decoded to FP32, times 64
+  uint8_t a[AROWS * AROW];
 };
 
 constexpr int WCH = NT * CHUNKS / 256;          // code chunks per thread
-constexpr int SCH = NT * SB / 16 / 256 > 0 ? NT * SB / 16 / 256 : 1;
 
 // Code chunk c of weight row `row` (K-elements 32c .. 32c+31) sits at
 // woff(row, c) with its four dwords reordered [d0 d2 d1 d3], where d0/d1 are
 // the low/high halves of group 2c and d2/d3 those of group 2c+1: the lane
 // that feeds MFMA K-half h then reads both groups' slices as one 8-byte word.
 __device__ __forceinline__ int woff(int row, int chunk) {
-  return row * ROWB + ((chunk ^ (row & (CHUNKS - 1))) << 4);
+  return row * ROWB + ((chunk ^ ((row >> 1) & (CHUNKS - 1))) << 4);
 }
 
 template <int MT>
 struct RangeRegs {
-  static constexpr int ACH = MT * (KR / 16) / 256;  // token chunks per thread
+  static constexpr int ACH = (MT * (KR / 16) + 255) / 256;  // token chunks per thread
   u32x4 w[WCH];
-  u32x4 s[SCH];
+  u32x2 s;         // 8 scale bytes: row tid / 2, groups 8 (tid % 2) .. +7
   u32x4 a[ACH];
 };
 
 // loads of K range [k0, k0 + klen) of this workgroup's weight tile and tokens
-template <int MT>
+template <int MT, bool SFAST>
 __device__ __forceinline__ void range_load(const W4A8Args &p, int n0, int k0, int klen, int tid,
                                            RangeRegs<MT> &r) {
   constexpr int ACH = RangeRegs<MT>::ACH;
@@ -87,24 +87,26 @@ __device__ __forceinline__ void range_load(const W4A8Args &p, int n0, int k0, in
     const u32x4 v = *(const u32x4 *)(p.wq + (int64_t)n * (p.K / 2) + k0 / 2 + (in ? ch : 0) * 16);
     r.w[i] = in ? v : u32x4{0, 0, 0, 0};
   }
-#pragma unroll
-  for (int i = 0; i < SCH; ++i) {
-    const int c = tid + 256 * i, row = c / (SB / 16), ch = c % (SB / 16);
+  {
+    static_assert(SB == 16, "one scale row per thread pair");
+    const int row = tid >> 1, q = tid & 1;
     const int n = n0 + row < p.N ? n0 + row : p.N - 1;
-    const bool in = row < NT && ch * 256 < klen;
-    u32x4 v = {0, 0, 0, 0};
-    if ((G % 16) == 0) {
-      const u32x4 x = *(const u32x4 *)(p.ws + (int64_t)n * G + k0 / 16 + (in ? ch : 0) * 16);
-      v = in ? x : v;
-    } else if (in) {
-      uint32_t b[4] = {0, 0, 0, 0};
-      for (int e = 0; e < 16; ++e) {
-        const int g = k0 / 16 + ch * 16 + e;
-        if (g < G) b[e >> 2] |= (uint32_t)p.ws[(int64_t)n * G + g] << (8 * (e & 3));
+    const bool in = 128 * q < klen;              // groups 8q.. of this range exist
+    const uint8_t *srow = p.ws + (int64_t)n * G + k0 / 16;
+    if constexpr (SFAST) {  // K % 256 == 0: 8-byte aligned scale runs
+      const u32x2 x = *(const u32x2 *)(srow + (in ? 8 * q : 0));
+      r.s = in ? x : u32x2{0, 0};
+    } else {                // K % 32 == 0: 2-byte aligned, loaded in pairs
+      uint32_t b[2] = {0, 0};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int g = 8 * q + 2 * e;             // within the range
+        const bool ok = 16 * g < klen;
+        const uint32_t v = *(const uint16_t *)(srow + (ok ? g : 0));
+        b[e >> 1] |= (ok ? v : 0u) << (16 * (e & 1));
       }
-      v = u32x4{b[0], b[1], b[2], b[3]};
+      r.s = u32x2{b[0], b[1]};
     }
-    r.s[i] = v;
   }
 #pragma unroll
   for (int i = 0; i < ACH; ++i) {
@@ -125,52 +127,60 @@ __device__ __forceinline__ void range_store(Tile<MT> &tile, int M, int tid, cons
     const u32x4 v = r.w[i];
     *(u32x4 *)(tile.w + woff(row, ch)) = u32x4{v[0], v[2], v[1], v[3]};
   }
+  {
+    const int row = tid >> 1, q = tid & 1;
+    float *dst = tile.s + row * SROWF + 8 * q;
 #pragma unroll
-  for (int i = 0; i < SCH; ++i) {
-    const int c = tid + 256 * i, row = c / (SB / 16), ch = c % (SB / 16);
-    if (c < NT * SB / 16) {
-      uint32_t *dst = (uint32_t *)(tile.s + row * SROW + ch * 16);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) dst[j] = r.s[i][j];
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t w = r.s[j >> 1] >> (16 * (j & 1));
+      *(f32x2 *)(dst + 2 * j) = f32x2{e4m3_x64_to_f32_nan(w & 0xFFu), e4m3_x64_to_f32_nan((w >> 8) & 0xFFu)};
     }
   }
 #pragma unroll
   for (int i = 0; i < ACH; ++i) {
+    // (rows t >= M hold zeros; the tile has a row for every chunk loaded, so
+    // the store needs no guard that a load could be sunk into)
     const int c = tid + 256 * i, t = c / (KR / 16), g = c % (KR / 16);
-    if (t < M) {
-      // each 8-byte slice in even/odd byte order (the converted weight codes
-      // come out in that order); the slices of groups 2c and 2c+1 that one
-      // MFMA K-half reads are placed side by side: [lo(2c) lo(2c+1) | hi(2c) hi(2c+1)]
-      const uint64_t lo = e4m3x8_even_odd((uint64_t)r.a[i][0] | ((uint64_t)r.a[i][1] << 32));
-      const uint64_t hi = e4m3x8_even_odd((uint64_t)r.a[i][2] | ((uint64_t)r.a[i][3] << 32));
-      uint8_t *dst = tile.a + t * AROW + 32 * (g >> 1) + 8 * (g & 1);
-      *(uint64_t *)dst = lo;
-      *(uint64_t *)(dst + 16) = hi;
-    }
+    // each 8-byte slice in even/odd byte order (the converted weight codes
+    // come out in that order); the slices of groups 2c and 2c+1 that one
+    // MFMA K-half reads are placed side by side: [lo(2c) lo(2c+1) | hi(2c) hi(2c+1)]
+    const uint64_t lo = e4m3x8_even_odd((uint64_t)r.a[i][0] | ((uint64_t)r.a[i][1] << 32));
+    const uint64_t hi = e4m3x8_even_odd((uint64_t)r.a[i][2] | ((uint64_t)r.a[i][3] << 32));
+    uint8_t *dst = tile.a + t * AROW + 32 * (g >> 1) + 8 * (g & 1);
+    *(uint64_t *)dst = lo;
+    *(uint64_t *)(dst + 16) = hi;
   }
 }
 
 // np pairs of 16-element groups (2 groups per code chunk) from the LDS tile
+// QUADS = accumulator quads in use (8 tokens each); 0 means one token: only
+// register 0 (token 0 in the lanes of K-half 0) is updated and stored.
+template <int QUADS>
+struct Acc {
+  static constexpr int MT = QUADS == 0 ? 8 : 8 * QUADS;   // token rows in the LDS tile
+  static constexpr int NREG = QUADS == 0 ? 1 : 4 * QUADS; // accumulator registers in use
+};
+
 template <int QUADS, bool FULL>
-__device__ __forceinline__ void compute_range(const Tile<8 * QUADS> &tile, int row, int trow, int h, int np,
+__device__ __forceinline__ void compute_range(const Tile<Acc<QUADS>::MT> &tile, int row, int trow, int h, int np,
                                               f32x16 &acc) {
-  const uint8_t *wrow = tile.w + row * ROWB + 8 * h;
+  const uint8_t *wtile = tile.w + 8 * h;
   const uint8_t *arow = tile.a + trow * AROW + 16 * h;
-  const uint8_t *srow = tile.s + row * SROW;
+  const float *srow = tile.s + row * SROWF;
   const f32x16 zero = {0};
   auto pair = [&](int c) {
-    const uint64_t cw = *(const uint64_t *)(wrow + ((c ^ (row & (CHUNKS - 1))) << 4));
+    const uint64_t cw = *(const uint64_t *)(wtile + woff(row, c));
     const u32x4 av = *(const u32x4 *)(arow + 32 * c);
-    const uint32_t sc = *(const uint16_t *)(srow + 2 * c);
-    const float s0 = e4m3_x64_to_f32(sc & 0xFFu), s1 = e4m3_x64_to_f32(sc >> 8);
+    const f32x2 sc = *(const f32x2 *)(srow + 2 * c);
+    const float s0 = sc[0], s1 = sc[1];
     const uint64_t a0 = (uint64_t)av[0] | ((uint64_t)av[1] << 32);
     const uint64_t a1 = (uint64_t)av[2] | ((uint64_t)av[3] << 32);
     const f32x16 p0 = mfma_fp8(a0, nvfp4x8_to_e4m3x8((uint32_t)cw), zero);
     const f32x16 p1 = mfma_fp8(a1, nvfp4x8_to_e4m3x8((uint32_t)(cw >> 32)), zero);
 #pragma unroll
-    for (int r = 0; r < 4 * QUADS; ++r) acc[r] = __builtin_fmaf(s0, p0[r], acc[r]);
+    for (int r = 0; r < Acc<QUADS>::NREG; ++r) acc[r] = __builtin_fmaf(s0, p0[r], acc[r]);
 #pragma unroll
-    for (int r = 0; r < 4 * QUADS; ++r) acc[r] = __builtin_fmaf(s1, p1[r], acc[r]);
+    for (int r = 0; r < Acc<QUADS>::NREG; ++r) acc[r] = __builtin_fmaf(s1, p1[r], acc[r]);
   };
   if constexpr (FULL) {
 #pragma unroll
@@ -181,7 +191,7 @@ __device__ __forceinline__ void compute_range(const Tile<8 * QUADS> &tile, int r
 }
 
 template <int QUADS>
-__device__ __forceinline__ void compute_any(const Tile<8 * QUADS> &tile, int row, int trow, int h, int klen,
+__device__ __forceinline__ void compute_any(const Tile<Acc<QUADS>::MT> &tile, int row, int trow, int h, int klen,
                                             f32x16 &acc) {
   if (klen == KR)
     compute_range<QUADS, true>(tile, row, trow, h, CHUNKS, acc);
@@ -189,34 +199,41 @@ __device__ __forceinline__ void compute_any(const Tile<8 * QUADS> &tile, int row
     compute_range<QUADS, false>(tile, row, trow, h, klen / 32, acc);
 }
 
-template <int QUADS>
+template <int QUADS, bool SFAST>
 __global__ __launch_bounds__(256) void w4a8_decode_kernel(W4A8Args p, int ks, float *part) {
-  __shared__ __attribute__((aligned(16))) Tile<8 * QUADS> tile;
+  constexpr int MT = Acc<QUADS>::MT;
+  __shared__ __attribute__((aligned(16))) Tile<MT> tile;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
   const int nt = blockIdx.x, kc = blockIdx.y;
   const int n0 = nt * NT;
   const int nrange = (p.K + KR - 1) / KR;
   const int rbeg = kc * RPW;
-  const bool two = rbeg + 1 < nrange;  // RPW == 2
+  const int rend = rbeg + RPW < nrange ? rbeg + RPW : nrange;
 
   const int row = wave * 32 + l32;
   const int trow = l32 < p.M ? l32 : 0;
   f32x16 acc = {0};
 
-  // both ranges' loads go out at once; the second lands while the first computes
-  const int k0a = rbeg * KR, klena = p.K - k0a < KR ? p.K - k0a : KR;
-  const int k0b = two ? k0a + KR : k0a, klenb = p.K - k0b < KR ? p.K - k0b : KR;
-  RangeRegs<8 * QUADS> ra, rb;
-  range_load(p, n0, k0a, klena, tid, ra);
-  range_load(p, n0, k0b, klenb, tid, rb);
-  range_store(tile, p.M, tid, ra);
-  __syncthreads();
-  compute_any<QUADS>(tile, row, trow, h, klena, acc);
-  if (two) {
+  // All of the workgroup's ranges (at most RPW) are requested at once into
+  // register buffers, so the whole weight stream is in flight from the start;
+  // each range is then staged through the one LDS tile and computed as it
+  // lands (loads complete in issue order).  A range past the run is requested
+  // with length 0: all of its data is masked and only each row's first chunk
+  // is touched.
+  auto klen = [&](int rg) {
+    return rg >= rend ? 0 : (p.K - rg * KR < KR ? p.K - rg * KR : KR);
+  };
+  auto kstart = [&](int rg) { return (rg < rend ? rg : rend - 1) * KR; };
+  RangeRegs<MT> rr[RPW];
+#pragma unroll
+  for (int j = 0; j < RPW; ++j) range_load<MT, SFAST>(p, n0, kstart(rbeg + j), klen(rbeg + j), tid, rr[j]);
+#pragma unroll
+  for (int j = 0; j < RPW; ++j) {
+    if (rbeg + j >= rend) break;
+    if (j > 0) __syncthreads();
+    range_store(tile, p.M, tid, rr[j]);
     __syncthreads();
-    range_store(tile, p.M, tid, rb);
-    __syncthreads();
-    compute_any<QUADS>(tile, row, trow, h, klenb, acc);
+    compute_any<QUADS>(tile, row, trow, h, klen(rbeg + j), acc);
   }
 
   const int n = n0 + row;
@@ -224,7 +241,7 @@ __global__ __launch_bounds__(256) void w4a8_decode_kernel(W4A8Args p, int ks, fl
   if (ks == 1) {
     const float sw = *p.Sw;
 #pragma unroll
-    for (int r = 0; r < 4 * QUADS; ++r) {
+    for (int r = 0; r < Acc<QUADS>::NREG; ++r) {
       const int t = acc_row(r, lane);
       if (t >= p.M) continue;
       const float v = acc[r] * (p.atok[t] * sw);
@@ -236,7 +253,7 @@ __global__ __launch_bounds__(256) void w4a8_decode_kernel(W4A8Args p, int ks, fl
     return;
   }
 #pragma unroll
-  for (int r = 0; r < 4 * QUADS; ++r) {
+  for (int r = 0; r < Acc<QUADS>::NREG; ++r) {
     const int t = acc_row(r, lane);
     if (t < p.M) part[((int64_t)kc * p.M + t) * p.N + n] = acc[r];
   }
@@ -265,21 +282,21 @@ __global__ __launch_bounds__(64) void w4a8_splitk_reduce(W4A8Args p, int ks, con
     ((uint16_t *)p.C)[i] = (uint16_t)f32_to_bf16_rne(v);
 }
 
-int splits(int K) {
-  const int nrange = (K + KR - 1) / KR;
-  return (nrange + RPW - 1) / RPW;
-}
+int splits(int64_t K) { return (int)(((K + KR - 1) / KR + RPW - 1) / RPW); }
 
 template <int QUADS>
 void launch_one(const W4A8Args &p, int ks, float *part, hipStream_t stream) {
   dim3 grid((p.N + NT - 1) / NT, ks);
-  hipLaunchKernelGGL((w4a8_decode_kernel<QUADS>), grid, dim3(256), 0, stream, p, ks, part);
+  if (p.K % 256 == 0)
+    hipLaunchKernelGGL((w4a8_decode_kernel<QUADS, true>), grid, dim3(256), 0, stream, p, ks, part);
+  else
+    hipLaunchKernelGGL((w4a8_decode_kernel<QUADS, false>), grid, dim3(256), 0, stream, p, ks, part);
 }
 
 }  // namespace
 
 size_t w4a8_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  const int ks = splits((int)K);
+  const int ks = splits(K);
   if (ks <= 1) return 0;
   const int64_t Ms = M < MS ? M : MS;
   return (size_t)ks * (size_t)Ms * (size_t)N * sizeof(float);
@@ -299,7 +316,8 @@ hipError_t launch_w4a8(const W4A8Args &p0, hipStream_t stream) {
     if (p.M > 24) launch_one<4>(p, ks, part, stream);
     else if (p.M > 16) launch_one<3>(p, ks, part, stream);
     else if (p.M > 8) launch_one<2>(p, ks, part, stream);
-    else launch_one<1>(p, ks, part, stream);
+    else if (p.M > 1) launch_one<1>(p, ks, part, stream);
+    else launch_one<0>(p, ks, part, stream);
     if (ks > 1) {
       const int64_t mn = (int64_t)p.M * p.N;
       hipLaunchKernelGGL(w4a8_splitk_reduce, dim3((unsigned)((mn + 63) / 64)), dim3(64), 0,
