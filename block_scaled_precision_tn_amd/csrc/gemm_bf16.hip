@@ -8,21 +8,53 @@
 //           are the declared ones; the FP32 tensor scale S_w is applied in the
 //           epilogue (an arbitrary FP32 value would not be exact in BF16).
 //
-// Workgroup: 256 threads (4 waves, 2x2), tile 128 x 128 x 64, wave tile
-// 64 x 64 = 2 x 2 blocks of v_mfma_f32_32x32x16_bf16.  Operands are staged
-// through LDS (double-buffered) in 16-byte chunks whose position within a
-// 128-byte row is XOR-swizzled by the row index, so the MFMA fragment reads
-// (32 rows x one chunk) hit distinct banks.
+// Workgroup: 512 threads (8 waves, 4 along M x 2 along N), tile 256 x 128,
+// K staged 64 at a time; wave tile 64 x 64 = 2 x 2 blocks of
+// v_mfma_f32_32x32x16_bf16; one workgroup per CU.
+//   * BF16 operands go from global memory straight into LDS (16-byte
+//     global_load_lds: lane i's bytes land at the instruction's LDS base +
+//     16 i), three stages deep, so two stages are in flight while one is
+//     computed and no registers are spent on staging.  The lane -> global
+//     chunk assignment realises the XOR swizzle of the LDS rows (see swz), so
+//     the MFMA fragment reads (32 rows x one chunk) hit distinct banks.
+//   * NVFP4 weights (W4A16) are loaded to registers one stage ahead, widened
+//     to BF16 and written to the same LDS layout.
+//   * Tiles are assigned XCD by XCD (see xcd_tile) so the workgroups sharing
+//     an L2 share A and W panels.
 #include "common.h"
 #include "kernels.h"
 
 namespace mg {
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int ROWB = BK * 2;  // bytes per LDS row (64 BF16)
+constexpr int BM = 256, BN = 128, BK = 64;
+constexpr int NTHR = 512;            // 8 waves
+constexpr int NSTAGE = 3;            // LDS ring depth
+constexpr int ROWB = BK * 2;         // bytes per LDS row (64 BF16)
+constexpr int STAGE_A = BM * ROWB, STAGE_W = BN * ROWB;
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * ROWB + ((chunk ^ (row & 7)) << 4); }
+typedef __attribute__((address_space(1))) void gvoid;
+typedef __attribute__((address_space(3))) void lvoid;
+
+// 16-byte chunk `chunk` of tile row `row`: rows are 128 bytes, and the chunk
+// is XOR-ed with (row / 2) % 8, so any 16 consecutive rows read at one chunk
+// index cover 16 distinct 16-byte bank groups of the 256-byte bank window.
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return row * ROWB + ((chunk ^ ((row >> 1) & 7)) << 4);
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14; expcnt (6:4) and lgkmcnt (11:8) at maximum)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// s_waitcnt lgkmcnt(0) only
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt(63 | (3 << 14) | (7 << 4) | (0 << 8));
+}
 
 // E2M1 code (low 4 bits) -> FP32 value
 __device__ __forceinline__ float e2m1_to_f32(uint32_t c) {
@@ -35,90 +67,92 @@ __device__ __forceinline__ float e2m1_to_f32(uint32_t c) {
   return __builtin_bit_cast(float, bits);
 }
 
-template <bool WQ>
-struct Stage {
-  u32x4 a[4];
-  u32x4 w[4];     // BF16 W chunks (WQ = false) or NVFP4 codes in w[0] (WQ = true)
-  uint32_t ws;    // WQ: 4 scale bytes of one W row
+// Issue the direct-to-LDS loads of one BF16 operand tile (R rows x 64 K) at
+// k0 into `lds`.  Each wave instruction fills 1 KB = 8 rows; lane i fills LDS
+// position (row 8b + i / 8, slot i % 8), which holds global chunk
+// slot ^ ((row / 2) % 8).  Rows past the matrix read its last row (never
+// stored); chunks past K read the row's last chunk (zeroed by fix_k_tail).
+template <int R>
+__device__ __forceinline__ void dma_tile(const uint16_t *src, int rows, int K, int r0, int k0,
+                                         uint8_t *lds, int wave, int lane) {
+  constexpr int BLOCKS = R / 8;                 // 1 KB blocks
+  constexpr int PER_WAVE = BLOCKS / (NTHR / 64);
+#pragma unroll
+  for (int j = 0; j < PER_WAVE; ++j) {
+    const int b = wave * PER_WAVE + j;
+    const int row = 8 * b + (lane >> 3), slot = lane & 7;
+    const int chunk = slot ^ ((row >> 1) & 7);
+    int grow = r0 + row;
+    grow = grow < rows ? grow : rows - 1;
+    int k = k0 + 8 * chunk;
+    k = k < K ? k : K - 8;
+    __builtin_amdgcn_global_load_lds((gvoid *)(src + (int64_t)grow * K + k),
+                                     (lvoid *)(lds + 1024 * b), 16, 0, 0);
+  }
+}
+
+// Zero the chunks of a staged tile that lie past K (only the last stage of a
+// K that is not a multiple of 64 has any).
+template <int R>
+__device__ __forceinline__ void fix_k_tail(uint8_t *lds, int K, int k0, int tid) {
+  for (int c = tid; c < R * 8; c += NTHR) {
+    const int row = c >> 3, chunk = c & 7;
+    if (k0 + 8 * chunk >= K) *(u32x4 *)(lds + swz(row, chunk)) = u32x4{0, 0, 0, 0};
+  }
+}
+
+struct WqRegs {
+  u32x4 codes;    // 32 codes (two groups) of one weight half-row (threads < 256)
+  uint32_t sc;    // their two scale bytes
 };
 
-template <bool WQ>
-__device__ __forceinline__ void load_stage(const Bf16Args &p, int m0, int n0, int k0, int tid,
-                                           Stage<WQ> &st) {
-  // A: 128 rows x 128 B = 1024 chunks of 16 B, 4 per thread
+__device__ __forceinline__ void wq_load(const Bf16Args &p, int n0, int k0, int tid, WqRegs &r) {
+  const uint8_t *wq = (const uint8_t *)p.w;
+  const int row = (tid & 255) >> 1, half = tid & 1;
+  int grow = n0 + row;
+  grow = grow < p.N ? grow : p.N - 1;
+  const int k = k0 + half * 32, kc = k < p.K ? k : p.K - 32;  // in-bounds address; data masked
+  const u32x4 v = *(const u32x4 *)(wq + (int64_t)grow * (p.K / 2) + kc / 2);
+  r.codes = k < p.K ? v : u32x4{0, 0, 0, 0};
+  const uint32_t sv = *(const uint16_t *)(p.ws + (int64_t)grow * (p.K / 16) + kc / 16);
+  r.sc = k < p.K ? sv : 0u;
+}
+
+// widen 32 codes (two groups) to BF16: value = e2m1 * e4m3(scale), exact
+__device__ __forceinline__ void wq_store(uint8_t *lw, int tid, const WqRegs &r) {
+  if (tid >= 256) return;
+  const int row = tid >> 1, half = tid & 1;
+  const float s0 = e4m3_to_f32(r.sc & 0xFFu), s1 = e4m3_to_f32((r.sc >> 8) & 0xFFu);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = tid + 256 * i, row = c >> 3, ch = c & 7;
-    int grow = m0 + row;
-    grow = grow < p.M ? grow : p.M - 1;
-    const int k = k0 + ch * 8;
-    st.a[i] = k < p.K ? *(const u32x4 *)(p.a + (int64_t)grow * p.K + k) : u32x4{0, 0, 0, 0};
-  }
-  if (!WQ) {
-    const uint16_t *w = (const uint16_t *)p.w;
+  for (int q = 0; q < 4; ++q) {      // 16 B of codes -> 4 chunks of 8 BF16
+    const uint32_t word = r.codes[q];
+    const float s = q < 2 ? s0 : s1;  // bytes 0..7: group 0, bytes 8..15: group 1
+    u32x4 out;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i, row = c >> 3, ch = c & 7;
-      int grow = n0 + row;
-      grow = grow < p.N ? grow : p.N - 1;
-      const int k = k0 + ch * 8;
-      st.w[i] = k < p.K ? *(const u32x4 *)(w + (int64_t)grow * p.K + k) : u32x4{0, 0, 0, 0};
+    for (int b = 0; b < 4; ++b) {
+      const uint32_t byte = (word >> (8 * b)) & 0xFFu;
+      const float lo = e2m1_to_f32(byte & 15u) * s, hi = e2m1_to_f32(byte >> 4) * s;
+      out[b] = (__builtin_bit_cast(uint32_t, lo) >> 16) | (__builtin_bit_cast(uint32_t, hi) & 0xFFFF0000u);
     }
-  } else {
-    // NVFP4: 128 rows x 32 B of codes = 256 chunks (one per thread) + 4 scale bytes per row
-    const uint8_t *wq = (const uint8_t *)p.w;
-    const int row = tid >> 1, half = tid & 1;
-    int grow = n0 + row;
-    grow = grow < p.N ? grow : p.N - 1;
-    const int k = k0 + half * 32;
-    st.w[0] = k < p.K ? *(const u32x4 *)(wq + (int64_t)grow * (p.K / 2) + k / 2) : u32x4{0, 0, 0, 0};
-    const uint16_t *s16 = (const uint16_t *)(p.ws + (int64_t)grow * (p.K / 16) + k / 16);
-    st.ws = k < p.K ? (uint32_t)s16[0] : 0u;  // 2 groups of this half-row
+    *(u32x4 *)(lw + swz(row, half * 4 + q)) = out;
   }
 }
 
 template <bool WQ>
-__device__ __forceinline__ void store_stage(uint8_t *la, uint8_t *lw, int tid, const Stage<WQ> &st) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = tid + 256 * i, row = c >> 3, ch = c & 7;
-    *(u32x4 *)(la + swz(row, ch)) = st.a[i];
-  }
-  if (!WQ) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i, row = c >> 3, ch = c & 7;
-      *(u32x4 *)(lw + swz(row, ch)) = st.w[i];
-    }
-  } else {
-    // widen 32 codes (two groups) to BF16: value = e2m1 * e4m3(scale), exact
-    const int row = tid >> 1, half = tid & 1;
-    const float s0 = e4m3_to_f32(st.ws & 0xFFu), s1 = e4m3_to_f32((st.ws >> 8) & 0xFFu);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {      // 16 B of codes -> 4 chunks of 8 BF16
-      const uint32_t word0 = st.w[0][q];
-      const float s = q < 2 ? s0 : s1;  // bytes 0..7: group 0, bytes 8..15: group 1
-      u32x4 out;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const uint32_t byte = (word0 >> (8 * b)) & 0xFFu;
-        const float lo = e2m1_to_f32(byte & 15u) * s, hi = e2m1_to_f32(byte >> 4) * s;
-        out[b] = (__builtin_bit_cast(uint32_t, lo) >> 16) | (__builtin_bit_cast(uint32_t, hi) & 0xFFFF0000u);
-      }
-      *(u32x4 *)(lw + swz(row, half * 4 + q)) = out;
-    }
-  }
-}
-
-template <bool WQ>
-__global__ __launch_bounds__(256, 2) void bf16_gemm_kernel(Bf16Args p) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BM * ROWB];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_w[2][BN * ROWB];
+__global__ __launch_bounds__(NTHR, 1) void bf16_gemm_kernel(Bf16Args p) {
+  // the three ring slots are separate arrays so the compiler can tell the
+  // loads landing in one slot from the reads of another (and does not wait
+  // for loads it does not need)
+  __shared__ __attribute__((aligned(1024))) uint8_t la0[STAGE_A], la1[STAGE_A], la2[STAGE_A];
+  __shared__ __attribute__((aligned(1024))) uint8_t lw0[STAGE_W], lw1[STAGE_W], lw2[STAGE_W];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1, h = lane >> 5, l32 = lane & 31;
-  const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
+  int tm, tn;
+  xcd_tile(blockIdx.x, (p.M + BM - 1) / BM, (p.N + BN - 1) / BN, tm, tn);
+  const int n0 = tn * BN, m0 = tm * BM;
   const int S = (p.K + BK - 1) / BK;
+  const uint16_t *wb = (const uint16_t *)p.w;
 
   f32x16 acc[2][2];
 #pragma unroll
@@ -126,30 +160,66 @@ __global__ __launch_bounds__(256, 2) void bf16_gemm_kernel(Bf16Args p) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{0};
 
-  Stage<WQ> st;
-  load_stage<WQ>(p, m0, n0, 0, tid, st);
-  store_stage<WQ>(lds_a[0], lds_w[0], tid, st);
-  __syncthreads();
+  // loads of stage t into a ring slot (stages past the end reload the last
+  // one: same addresses, never computed)
+  auto issue = [&](int t, uint8_t *la, uint8_t *lw) {
+    const int tt = t < S ? t : S - 1;
+    dma_tile<BM>(p.a, p.M, p.K, m0, tt * BK, la, wave, lane);
+    if (!WQ) dma_tile<BN>(wb, p.N, p.K, n0, tt * BK, lw, wave, lane);
+  };
+  // direct loads per thread per stage (A, then W unless it is NVFP4)
+  constexpr int LOADS = BM / 8 / (NTHR / 64) + (WQ ? 0 : BN / 8 / (NTHR / 64));
 
-  for (int s = 0; s < S; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < S) load_stage<WQ>(p, m0, n0, (s + 1) * BK, tid, st);
+  WqRegs wr;
+  // one stage: stage s sits in (la, lw); stage s+2 is issued into (na, nw),
+  // the slot stage s-1 used
+  auto step = [&](int s, uint8_t *la, uint8_t *lw, uint8_t *na, uint8_t *nw) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (WQ) {
+      // W of stage s from registers (loaded a stage ahead); the slot was last
+      // read by stage s - 3, which every wave finished before the previous barrier
+      wq_store(lw, tid, wr);
+      wq_load(p, n0, (s + 1) * BK, tid, wr);
+    }
+    // stage s has landed once at most stage s+1's loads are outstanding
+    // (the W4A16 register loads of stage s+1 were issued after them); LDS
+    // writes of this thread are complete once lgkmcnt is 0.  The barrier is
+    // the bare s_barrier: a fenced one would wait for every load in flight.
+    wait_vmcnt<WQ ? LOADS + 2 : LOADS>();
+    if (s == S - 1 && p.K % BK != 0) {
+      wait_vmcnt<0>();
+      fix_k_tail<BM>(la, p.K, s * BK, tid);
+      if (!WQ) fix_k_tail<BN>(lw, p.K, s * BK, tid);
+    }
+    wait_lgkm0();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    issue(s + 2, na, nw);
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
       u32x4 fa[2], fw[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        fa[i] = *(const u32x4 *)(lds_a[buf] + swz(wm * 64 + i * 32 + l32, 2 * kk + h));
-        fw[i] = *(const u32x4 *)(lds_w[buf] + swz(wn * 64 + i * 32 + l32, 2 * kk + h));
+        fa[i] = *(const u32x4 *)(la + swz(wm * 64 + i * 32 + l32, 2 * kk + h));
+        fw[i] = *(const u32x4 *)(lw + swz(wn * 64 + i * 32 + l32, 2 * kk + h));
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = mfma_bf16(fa[i], fw[j], acc[i][j]);
     }
-    if (s + 1 < S) store_stage<WQ>(lds_a[buf ^ 1], lds_w[buf ^ 1], tid, st);
-    __syncthreads();
+  };
+  if (WQ) wq_load(p, n0, 0, tid, wr);
+  issue(0, la0, lw0);
+  issue(1, la1, lw1);
+  for (int s = 0; s < S; s += 3) {
+    step(s, la0, lw0, la2, lw2);
+    if (s + 1 >= S) break;
+    step(s + 1, la1, lw1, la0, lw0);
+    if (s + 2 >= S) break;
+    step(s + 2, la2, lw2, la1, lw1);
   }
+  wait_vmcnt<0>();
 
   const float gs = WQ ? *p.Sw : 1.0f;
 #pragma unroll
@@ -174,11 +244,11 @@ __global__ __launch_bounds__(256, 2) void bf16_gemm_kernel(Bf16Args p) {
 }  // namespace
 
 hipError_t launch_bf16(const Bf16Args &p, hipStream_t stream) {
-  dim3 grid((p.N + BN - 1) / BN, (p.M + BM - 1) / BM);
+  dim3 grid(((p.N + BN - 1) / BN) * ((p.M + BM - 1) / BM));
   if (p.w_nvfp4)
-    hipLaunchKernelGGL(bf16_gemm_kernel<true>, grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(bf16_gemm_kernel<true>, grid, dim3(NTHR), 0, stream, p);
   else
-    hipLaunchKernelGGL(bf16_gemm_kernel<false>, grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(bf16_gemm_kernel<false>, grid, dim3(NTHR), 0, stream, p);
   return hipGetLastError();
 }
 
