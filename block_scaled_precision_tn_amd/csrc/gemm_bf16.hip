@@ -212,13 +212,16 @@ __global__ __launch_bounds__(NTHR, 1) void bf16_gemm_kernel(Bf16Args p) {
   if (WQ) wq_load(p, n0, 0, tid, wr);
   issue(0, la0, lw0);
   issue(1, la1, lw1);
-  for (int s = 0; s < S; s += 3) {
+  // whole ring turns, then the last one or two stages: the loop has a single
+  // exit, which keeps each accumulator in one set of registers
+  const int full = S - S % 3;
+  for (int s = 0; s < full; s += 3) {
     step(s, la0, lw0, la2, lw2);
-    if (s + 1 >= S) break;
     step(s + 1, la1, lw1, la0, lw0);
-    if (s + 2 >= S) break;
     step(s + 2, la2, lw2, la1, lw1);
   }
+  if (S % 3 >= 1) step(full, la0, lw0, la2, lw2);
+  if (S % 3 == 2) step(full + 1, la1, lw1, la0, lw0);
   wait_vmcnt<0>();
 
   const float gs = WQ ? *p.Sw : 1.0f;

@@ -32,7 +32,6 @@ constexpr int BM = 128;       // rows (routing entries) per tile
 constexpr int BNI = 64;       // intermediate columns per gate/up tile (x2 rows of w13)
 constexpr int BNH = 128;      // hidden columns per down tile
 constexpr int BK = 64;        // K per LDS stage (two 32-element scale blocks)
-constexpr int CROW = 80;      // LDS bytes per row of codes: 64 + 16 pad (bank spread)
 
 struct Layout {
   size_t counts, meta, sorted, tile_e, tile_r, tile_n, hq, hs, outf, total;
@@ -121,84 +120,117 @@ __global__ __launch_bounds__(256) void k_place(const int32_t *ids, int R, int E,
 }
 
 // ------------------------------------------------------- MX GEMM mainloop
-// A: 128 rows (row pointers per loading thread), B: 128 rows; both MXFP8
-// with K = Ktot.  Wave (wm, wn) computes rows wm*64 + [0,64) against the two
-// 32-row B slabs bsel[0], bsel[1] (LDS row offsets); acc[i][j] is the 32x32
-// block (A slab i, B slab j).
-struct MxOperandPtrs {
-  const uint8_t *a_code[2];   // this thread's two A chunk rows (code row base)
-  const uint8_t *b_code[2];
-  const uint8_t *sc_row;      // this thread's scale row (A if tid < 128, else B)
-  bool a_ok[2], b_ok[2], sc_ok;
+// A: 128 rows, B: 128 rows, both MXFP8 with K = Ktot (a multiple of 64).
+// Wave (wm, wn) computes rows wm*64 + [0,64) against the two 32-row B slabs
+// bsel[0], bsel[1]; acc[i][j] is the 32x32 block (A slab i, B slab j).
+//
+// Operands go from global memory straight into LDS (global_load_lds: lane i
+// of an instruction lands at its LDS base + i * size), three stages of 64 K
+// deep, so two stages are in flight while one is computed.  Per stage and
+// operand a 128 x 64-byte code tile, rows XOR-swizzled in 16-byte chunks (see
+// mx_off) so MFMA fragment reads hit distinct banks, and the rows' two E8M0
+// scale bytes (A rows, then B rows; a 2-byte direct load fills one LDS dword
+// per lane, low half).  A rows are gathered: every lane holds the global row
+// pointers of the rows it loads.
+typedef __attribute__((address_space(1))) void gvoid;
+typedef __attribute__((address_space(3))) void lvoid;
+
+constexpr int MX_CODE = BM * BK;          // bytes of one operand's codes per stage
+constexpr int MX_SC = 2 * BM * 4;         // scale dwords per stage (A rows then B rows)
+
+// chunk `chunk` (16 bytes) of 64-byte row `row`: XOR-ed with (row / 4) % 4,
+// so 16 consecutive rows at one chunk index cover all 64 LDS banks
+__device__ __forceinline__ int mx_off(int row, int chunk) {
+  return row * BK + ((chunk ^ ((row >> 2) & 3)) << 4);
+}
+
+template <int N>
+__device__ __forceinline__ void mx_wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+struct MxRows {
+  const uint8_t *a[2], *b[2];   // code rows this lane loads: rows 16 (2 wave + j) + lane / 4
+  const uint8_t *s;             // scale row of row (64 wave + lane) % 128 (A if < 128, else B)
 };
 
-__device__ __forceinline__ int crow_off(int row, int chunk) { return row * CROW + chunk * 16; }
+// lane's loads of one stage at k0: 2 A + 2 B code chunks, 1 scale pair
+__device__ __forceinline__ void mx_issue(const MxRows &r, int k0, uint8_t *la, uint8_t *lb,
+                                         uint8_t *ls, int wave, int lane) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int blk = 2 * wave + j, row = 16 * blk + (lane >> 2), slot = lane & 3;
+    const int chunk = slot ^ ((row >> 2) & 3);
+    __builtin_amdgcn_global_load_lds((gvoid *)(r.a[j] + k0 + 16 * chunk), (lvoid *)(la + 1024 * blk), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((gvoid *)(r.b[j] + k0 + 16 * chunk), (lvoid *)(lb + 1024 * blk), 16, 0, 0);
+  }
+  __builtin_amdgcn_global_load_lds((gvoid *)(r.s + k0 / 32), (lvoid *)(ls + 256 * wave), 2, 0, 0);
+}
 
 template <int NB>
-__device__ __forceinline__ void mx_mainloop(const MxOperandPtrs &ptr, int Ktot, uint8_t *lds,
-                                            const int bsel[NB], f32x16 (&acc)[2][NB]) {
-  constexpr int STAGE = 2 * BM * CROW + 2 * BM * 2;
+__device__ __forceinline__ void mx_mainloop(const MxRows &rows, int Ktot, const int bsel[NB],
+                                            f32x16 (&acc)[2][NB]) {
+  // three ring slots as separate arrays: the compiler can tell loads landing
+  // in one slot from reads of another
+  __shared__ __attribute__((aligned(1024))) uint8_t a0[MX_CODE], a1[MX_CODE], a2[MX_CODE];
+  __shared__ __attribute__((aligned(1024))) uint8_t b0[MX_CODE], b1[MX_CODE], b2[MX_CODE];
+  __shared__ __attribute__((aligned(256))) uint8_t s0[MX_SC], s1[MX_SC], s2[MX_SC];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, h = lane >> 5, l32 = lane & 31;
   const int S = Ktot / BK;
+  constexpr int LOADS = 5;   // DMA instructions per lane per stage
 
-  u32x4 ra[2], rb[2];
-  uint32_t rs;
-  auto gload = [&](int s) {
-    const int k0 = s * BK;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + 256 * i, ch = c & 3;
-      ra[i] = ptr.a_ok[i] ? *(const u32x4 *)(ptr.a_code[i] + k0 + ch * 16) : u32x4{0, 0, 0, 0};
-      rb[i] = ptr.b_ok[i] ? *(const u32x4 *)(ptr.b_code[i] + k0 + ch * 16) : u32x4{0, 0, 0, 0};
-    }
-    rs = ptr.sc_ok ? (uint32_t) * (const uint16_t *)(ptr.sc_row + k0 / 32) : 0x7F7Fu;
-  };
-  auto lstore = [&](int buf) {
-    uint8_t *base = lds + buf * STAGE;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + 256 * i, row = c >> 2, ch = c & 3;
-      *(u32x4 *)(base + crow_off(row, ch)) = ra[i];
-      *(u32x4 *)(base + BM * CROW + crow_off(row, ch)) = rb[i];
-    }
-    *(uint16_t *)(base + 2 * BM * CROW + (tid >> 7) * (BM * 2) + (tid & 127) * 2) = (uint16_t)rs;
-  };
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int s = 0; s < S; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < S) gload(s + 1);
-    const uint8_t *base = lds + buf * STAGE;
+  auto step = [&](int s, const uint8_t *la, const uint8_t *lb, const uint8_t *ls,
+                  uint8_t *na, uint8_t *nb, uint8_t *ns) {
+    __builtin_amdgcn_sched_barrier(0);
+    // stage s has landed once at most stage s+1's loads are outstanding; the
+    // bare s_barrier (a fenced one would wait for every load in flight)
+    mx_wait_vmcnt<LOADS>();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    // stage s+2 into the slot stage s-1 used (every wave is past it); stages
+    // past the end reload the last one (never computed)
+    mx_issue(rows, (s + 2 < S ? s + 2 : S - 1) * BK, na, nb, ns, wave, lane);
     i32x8 fa[2], fb[NB];
     int sa[2], sb[NB];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int row = wm * 64 + i * 32 + l32;
-      const u32x4 lo = *(const u32x4 *)(base + crow_off(row, h));
-      const u32x4 hi = *(const u32x4 *)(base + crow_off(row, 2 + h));
+      const u32x4 lo = *(const u32x4 *)(la + mx_off(row, h));
+      const u32x4 hi = *(const u32x4 *)(la + mx_off(row, 2 + h));
       fa[i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-      sa[i] = base[2 * BM * CROW + row * 2 + h];
+      sa[i] = ls[4 * row + h];
     }
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       const int row = bsel[j] + l32;
-      const u32x4 lo = *(const u32x4 *)(base + BM * CROW + crow_off(row, h));
-      const u32x4 hi = *(const u32x4 *)(base + BM * CROW + crow_off(row, 2 + h));
+      const u32x4 lo = *(const u32x4 *)(lb + mx_off(row, h));
+      const u32x4 hi = *(const u32x4 *)(lb + mx_off(row, 2 + h));
       fb[j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-      sb[j] = base[2 * BM * CROW + BM * 2 + row * 2 + h];
+      sb[j] = ls[4 * (BM + row) + h];
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < NB; ++j) acc[i][j] = mfma_mx_fp8(fa[i], fb[j], acc[i][j], sa[i], sb[j]);
-    if (s + 1 < S) lstore(buf ^ 1);
-    __syncthreads();
+  };
+  mx_issue(rows, 0, a0, b0, s0, wave, lane);
+  mx_issue(rows, (1 < S ? 1 : 0) * BK, a1, b1, s1, wave, lane);
+  // whole ring turns, then the last one or two stages: the loop has a single
+  // exit, which keeps each accumulator in one set of registers
+  const int full = S - S % 3;
+  for (int s = 0; s < full; s += 3) {
+    step(s, a0, b0, s0, a2, b2, s2);
+    step(s + 1, a1, b1, s1, a0, b0, s0);
+    step(s + 2, a2, b2, s2, a1, b1, s1);
   }
+  if (S % 3 >= 1) step(full, a0, b0, s0, a2, b2, s2);
+  if (S % 3 == 2) step(full + 1, a1, b1, s1, a0, b0, s0);
+  mx_wait_vmcnt<0>();
+  // the slots are reused by the next tile only after this barrier
+  __builtin_amdgcn_s_barrier();
 }
-
-constexpr int MX_LDS = 2 * (2 * BM * CROW + 2 * BM * 2);
 
 // FP32 -> E4M3-FN byte, nearest even, saturating at +-448 (NaN -> 0x7F)
 __device__ __forceinline__ uint32_t f32_to_e4m3_rne_sat(float v) {
@@ -227,7 +259,6 @@ __global__ __launch_bounds__(256) void k_gateup(MoeArgs p, const int32_t *meta,
                                                 const int32_t *sorted, const int32_t *tile_e,
                                                 const int32_t *tile_r, const int32_t *tile_n,
                                                 uint8_t *hq, uint8_t *hs) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[MX_LDS];
   const int tile = blockIdx.y;
   if (tile >= meta[0]) return;
   const int e = tile_e[tile], r0 = tile_r[tile], nrows = tile_n[tile];
@@ -236,35 +267,34 @@ __global__ __launch_bounds__(256) void k_gateup(MoeArgs p, const int32_t *meta,
   const int wm = wave >> 1, wn = wave & 1, h = lane >> 5, l32 = lane & 31;
   const int H = p.H, I = p.I;
 
-  MxOperandPtrs ptr;
+  // A rows: gathered token rows (rows past the tile read the first entry's
+  // token: never stored); B rows 0..63: gate i0+row, 64..127: up I+i0+row-64
+  auto arow = [&](int row) {
+    const int t = sorted[r0 + (row < nrows ? row : 0)] / p.topk;
+    return p.xq + (int64_t)t * H;
+  };
+  auto brow = [&](int row) { return row < BNI ? i0 + row : I + i0 + (row - BNI); };
+  MxRows rows;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int c = tid + 256 * i, row = c >> 2;
-    ptr.a_ok[i] = row < nrows;
-    const int t = ptr.a_ok[i] ? sorted[r0 + row] / p.topk : 0;
-    ptr.a_code[i] = p.xq + (int64_t)t * H;
-    // B rows 0..63: gate i0+row, rows 64..127: up I+i0+row-64
-    const int brow = row < BNI ? i0 + row : I + i0 + (row - BNI);
-    ptr.b_ok[i] = true;
-    ptr.b_code[i] = p.w13q + ((int64_t)e * 2 * I + brow) * H;
+  for (int j = 0; j < 2; ++j) {
+    const int row = 16 * (2 * wave + j) + (lane >> 2);
+    rows.a[j] = arow(row);
+    rows.b[j] = p.w13q + ((int64_t)e * 2 * I + brow(row)) * H;
   }
   {
-    const int row = tid & 127;
-    if (tid < 128) {
-      ptr.sc_ok = row < nrows;
-      const int t = ptr.sc_ok ? sorted[r0 + row] / p.topk : 0;
-      ptr.sc_row = p.xs + (int64_t)t * (H / 32);
+    const int q = 64 * wave + lane, row = q & 127;
+    if (q < 128) {
+      const int t = sorted[r0 + (row < nrows ? row : 0)] / p.topk;
+      rows.s = p.xs + (int64_t)t * (H / 32);
     } else {
-      ptr.sc_ok = true;
-      const int brow = row < BNI ? i0 + row : I + i0 + (row - BNI);
-      ptr.sc_row = p.w13s + ((int64_t)e * 2 * I + brow) * (H / 32);
+      rows.s = p.w13s + ((int64_t)e * 2 * I + brow(row)) * (H / 32);
     }
   }
   f32x16 acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) acc[i][0] = acc[i][1] = f32x16{0};
   const int bsel[2] = {wn * 32, BNI + wn * 32};  // gate slab, up slab of the same columns
-  mx_mainloop<2>(ptr, H, lds, bsel, acc);
+  mx_mainloop<2>(rows, H, bsel, acc);
 
   // epilogue: h = silu(g) * u, MXFP8 block of 32 columns = this wave's 32 lanes
   const int col = i0 + wn * 32 + l32;
@@ -304,7 +334,6 @@ __global__ __launch_bounds__(256) void k_down(MoeArgs p, const int32_t *meta, co
                                               const int32_t *tile_e, const int32_t *tile_r,
                                               const int32_t *tile_n, const uint8_t *hq,
                                               const uint8_t *hs, float *outf) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[MX_LDS];
   const int tile = blockIdx.y;
   if (tile >= meta[0]) return;
   const int e = tile_e[tile], r0 = tile_r[tile], nrows = tile_n[tile];
@@ -313,30 +342,27 @@ __global__ __launch_bounds__(256) void k_down(MoeArgs p, const int32_t *meta, co
   const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31;
   const int H = p.H, I = p.I;
 
-  MxOperandPtrs ptr;
+  // A rows: sorted h rows (rows past the tile read its first row: never
+  // stored); B rows: w2[e] rows n0 + row (past H: the last row, never stored)
+  MxRows rows;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int c = tid + 256 * i, row = c >> 2;
-    ptr.a_ok[i] = row < nrows;
-    ptr.a_code[i] = hq + (int64_t)(r0 + (row < nrows ? row : 0)) * I;
-    ptr.b_ok[i] = n0 + row < H;
-    ptr.b_code[i] = p.w2q + ((int64_t)e * H + n0 + row) * I;
+  for (int j = 0; j < 2; ++j) {
+    const int row = 16 * (2 * wave + j) + (lane >> 2);
+    rows.a[j] = hq + (int64_t)(r0 + (row < nrows ? row : 0)) * I;
+    rows.b[j] = p.w2q + ((int64_t)e * H + (n0 + row < H ? n0 + row : H - 1)) * I;
   }
   {
-    const int row = tid & 127;
-    if (tid < 128) {
-      ptr.sc_ok = row < nrows;
-      ptr.sc_row = hs + (int64_t)(r0 + (row < nrows ? row : 0)) * (I / 32);
-    } else {
-      ptr.sc_ok = n0 + row < H;
-      ptr.sc_row = p.w2s + ((int64_t)e * H + n0 + row) * (I / 32);
-    }
+    const int q = 64 * wave + lane, row = q & 127;
+    if (q < 128)
+      rows.s = hs + (int64_t)(r0 + (row < nrows ? row : 0)) * (I / 32);
+    else
+      rows.s = p.w2s + ((int64_t)e * H + (n0 + row < H ? n0 + row : H - 1)) * (I / 32);
   }
   f32x16 acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) acc[i][0] = acc[i][1] = f32x16{0};
   const int bsel[2] = {wn * 64, wn * 64 + 32};
-  mx_mainloop<2>(ptr, I, lds, bsel, acc);
+  mx_mainloop<2>(rows, I, bsel, acc);
 
 #pragma unroll
   for (int i = 0; i < 2; ++i)
