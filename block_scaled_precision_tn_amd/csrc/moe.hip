@@ -11,17 +11,18 @@
 //     out[t] += ids weight * y   (FP32), then BF16
 //
 // Stream-ordered kernels:
-//   k_prep   zero the expert counters and the FP32 output accumulator
-//   k_count  per-expert histogram of the routing entries
-//   k_place  one workgroup per expert: row offset, stable compaction of that
-//            expert's (token, slot) entries in (token, slot) order, and its
-//            128-row tile list (so grouped GEMM grids need no host sync)
+//   k_prep   zero the expert counters
+//   k_count  per-expert histogram; each entry's rank within its expert
+//   k_scan   expert row offsets and the 128-row tile list (so the grouped
+//            GEMM grids need no host sync)
+//   k_scatter each entry's sorted row (entries grouped by expert)
 //   k_gateup grouped GEMM on the E8M0-scaled FP8 MFMA with gathered token
 //            rows; epilogue: GLU, MXFP8 re-quantisation of h (block amax by
 //            cross-lane max), h stored in expert-sorted order
 //   k_down   grouped GEMM of sorted h rows against w2[e]; epilogue: times the
-//            routing weight, FP32 atomic add into out[t]
-//   k_cast   FP32 -> BF16
+//            routing weight, stored FP32 per routed row (expert-sorted order)
+//   k_combine out[t] = sum over slots j = 0..topk-1, in order, of the stored
+//            rows of (t, j), then BF16 (deterministic: no atomics)
 #include "common.h"
 #include "kernels.h"
 
@@ -34,7 +35,7 @@ constexpr int BNH = 128;      // hidden columns per down tile
 constexpr int BK = 64;        // K per LDS stage (two 32-element scale blocks)
 
 struct Layout {
-  size_t counts, meta, sorted, tile_e, tile_r, tile_n, hq, hs, outf, total;
+  size_t counts, offs, meta, sorted, pos, tile_e, tile_r, tile_n, hq, hs, y, total;
   int R, maxtiles;
 };
 
@@ -46,76 +47,103 @@ Layout layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk) {
   L.maxtiles = (int)((L.R + BM - 1) / BM + E);
   size_t o = 0;
   L.counts = o; o += up256(sizeof(uint32_t) * (size_t)E);
+  L.offs = o;   o += up256(sizeof(int32_t) * (size_t)E);
   L.meta = o;   o += up256(sizeof(int32_t) * 4);                 // [0] = number of tiles
   L.sorted = o; o += up256(sizeof(int32_t) * (size_t)L.R);
+  L.pos = o;    o += up256(sizeof(int32_t) * (size_t)L.R);          // sorted row of each entry
   L.tile_e = o; o += up256(sizeof(int32_t) * (size_t)L.maxtiles);
   L.tile_r = o; o += up256(sizeof(int32_t) * (size_t)L.maxtiles);
   L.tile_n = o; o += up256(sizeof(int32_t) * (size_t)L.maxtiles);
   L.hq = o;     o += up256((size_t)L.R * (size_t)I);
   L.hs = o;     o += up256((size_t)L.R * (size_t)(I / 32));
-  L.outf = o;   o += up256(sizeof(float) * (size_t)T * (size_t)H);
+  L.y = o;      o += up256(sizeof(float) * (size_t)L.R * (size_t)H);  // weighted down rows
   L.total = o;
   return L;
 }
 
 // ---------------------------------------------------------------- routing
-__global__ void k_prep(uint32_t *counts, int E, float *outf, int64_t n) {
-  const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t step = (int64_t)gridDim.x * blockDim.x;
-  if (i0 < E) counts[i0] = 0u;
-  for (int64_t i = i0; i < n / 4; i += step) ((f32x4 *)outf)[i] = f32x4{0, 0, 0, 0};
+__global__ void k_prep(uint32_t *counts, int E) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < E) counts[i] = 0u;
 }
 
-__global__ void k_count(const int32_t *ids, int R, int E, uint32_t *counts) {
+// rank of each entry within its expert (arrival order); out-of-range ids are
+// dropped.  Row order within an expert does not change any result: every
+// row's GEMMs and re-quantisation are independent of the other rows.
+__global__ __launch_bounds__(1024) void k_count(const int32_t *ids, int R, int E,
+                                                uint32_t *counts, int32_t *rank) {
+  // ranks within the workgroup from LDS counters, then one global atomic per
+  // (workgroup, expert) reserves the workgroup's run of ranks
+  __shared__ uint32_t s_cnt[1024], s_base[1024];
+  const int tid = threadIdx.x, i = blockIdx.x * 1024 + tid;
+  if (tid < E) s_cnt[tid] = 0u;
+  __syncthreads();
+  const int e = i < R ? ids[i] : -1;
+  const bool ok = e >= 0 && e < E;
+  const uint32_t lr = ok ? atomicAdd(&s_cnt[e], 1u) : 0u;
+  __syncthreads();
+  if (tid < E && s_cnt[tid] != 0u) s_base[tid] = atomicAdd(&counts[tid], s_cnt[tid]);
+  __syncthreads();
+  if (i < R) rank[i] = ok ? (int32_t)(s_base[e] + lr) : -1;
+}
+
+// one workgroup: exclusive scans of the expert counts (row offsets) and of
+// their tile counts (tile list: expert, first row, rows)
+__global__ __launch_bounds__(256) void k_scan(const uint32_t *counts, int E, int32_t *offs,
+                                              int32_t *meta, int32_t *tile_e, int32_t *tile_r,
+                                              int32_t *tile_n) {
+  __shared__ int s_rows[256], s_tiles[256];
+  const int tid = threadIdx.x;
+  constexpr int PER = 4;                       // experts per thread (E <= 1024)
+  int rows[PER], tiles[PER], r = 0, t = 0;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int e = tid * PER + k;
+    const int c = e < E ? (int)counts[e] : 0;
+    rows[k] = c;
+    tiles[k] = (c + BM - 1) / BM;
+    r += c;
+    t += tiles[k];
+  }
+  s_rows[tid] = r;
+  s_tiles[tid] = t;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {          // inclusive scan over threads
+    const int ar = tid >= o ? s_rows[tid - o] : 0, at = tid >= o ? s_tiles[tid - o] : 0;
+    __syncthreads();
+    s_rows[tid] += ar;
+    s_tiles[tid] += at;
+    __syncthreads();
+  }
+  int rb = s_rows[tid] - r, tb = s_tiles[tid] - t;
+  if (tid == 255) meta[0] = s_tiles[255];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int e = tid * PER + k;
+    if (e < E) {
+      offs[e] = rb;
+      for (int q = 0; q < tiles[k]; ++q) {
+        tile_e[tb + q] = e;
+        tile_r[tb + q] = rb + q * BM;
+        tile_n[tb + q] = rows[k] - q * BM < BM ? rows[k] - q * BM : BM;
+      }
+    }
+    rb += rows[k];
+    tb += tiles[k];
+  }
+}
+
+// sorted row of each entry, and the entry of each sorted row
+__global__ void k_scatter(const int32_t *ids, int R, const int32_t *offs, int32_t *pos,
+                          int32_t *sorted) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < R) {
-    const int e = ids[i];
-    if (e >= 0 && e < E) atomicAdd(&counts[e], 1u);  // out-of-range ids are dropped
-  }
-}
-
-__global__ __launch_bounds__(256) void k_place(const int32_t *ids, int R, int E,
-                                               const uint32_t *counts, int32_t *meta,
-                                               int32_t *sorted, int32_t *tile_e,
-                                               int32_t *tile_r, int32_t *tile_n) {
-  __shared__ int s_wave[4];
-  __shared__ int s_base, s_tbase;
-  const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid == 0) {
-    int off = 0, tb = 0, tt = 0;
-    for (int q = 0; q < E; ++q) {
-      const int c = (int)counts[q];
-      const int nt = (c + BM - 1) / BM;
-      if (q < e) { off += c; tb += nt; }
-      tt += nt;
+    const int rk = pos[i];                     // rank from k_count, or -1
+    if (rk >= 0) {
+      const int p = offs[ids[i]] + rk;
+      pos[i] = p;
+      sorted[p] = i;
     }
-    s_base = off;
-    s_tbase = tb;
-    if (e == 0) meta[0] = tt;
-  }
-  __syncthreads();
-  const int base = s_base, cnt = (int)counts[e];
-  // tile list of this expert
-  for (int q = tid; q * BM < cnt; q += 256) {
-    tile_e[s_tbase + q] = e;
-    tile_r[s_tbase + q] = base + q * BM;
-    tile_n[s_tbase + q] = cnt - q * BM < BM ? cnt - q * BM : BM;
-  }
-  // stable compaction of entries routed to e, in entry order (token, slot)
-  int running = 0;
-  for (int c0 = 0; c0 < R; c0 += 256) {
-    const int i = c0 + tid;
-    const bool f = i < R && ids[i] == e;
-    const uint64_t bal = __ballot(f);
-    const int before = __builtin_popcountll(bal & ((1ull << lane) - 1ull));
-    if (lane == 0) s_wave[wave] = __builtin_popcountll(bal);
-    __syncthreads();
-    int woff = 0;
-    for (int w = 0; w < wave; ++w) woff += s_wave[w];
-    const int tot = s_wave[0] + s_wave[1] + s_wave[2] + s_wave[3];
-    if (f) sorted[base + running + woff + before] = i;
-    running += tot;
-    __syncthreads();
   }
 }
 
@@ -333,7 +361,7 @@ __global__ __launch_bounds__(256) void k_gateup(MoeArgs p, const int32_t *meta,
 __global__ __launch_bounds__(256) void k_down(MoeArgs p, const int32_t *meta, const int32_t *sorted,
                                               const int32_t *tile_e, const int32_t *tile_r,
                                               const int32_t *tile_n, const uint8_t *hq,
-                                              const uint8_t *hs, float *outf) {
+                                              const uint8_t *hs, float *y) {
   const int tile = blockIdx.y;
   if (tile >= meta[0]) return;
   const int e = tile_e[tile], r0 = tile_r[tile], nrows = tile_n[tile];
@@ -370,24 +398,29 @@ __global__ __launch_bounds__(256) void k_down(MoeArgs p, const int32_t *meta, co
     for (int r = 0; r < 16; ++r) {
       const int row = wm * 64 + i * 32 + acc_row(r, lane);
       if (row >= nrows) continue;
-      const int ent = sorted[r0 + row];
-      const int t = ent / p.topk;
-      const float w = p.tw[ent];
+      const float w = p.tw[sorted[r0 + row]];
+      float *yrow = y + (int64_t)(r0 + row) * H;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int n = n0 + wn * 64 + j * 32 + l32;
-        if (n < H) unsafeAtomicAdd(&outf[(int64_t)t * H + n], acc[i][j][r] * w);
+        if (n < H) yrow[n] = acc[i][j][r] * w;
       }
     }
 }
 
-__global__ void k_cast(const float *outf, uint16_t *out, int64_t n) {
-  const int64_t step = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n / 4; i += step) {
-    const f32x4 v = ((const f32x4 *)outf)[i];
-    u32x2 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-    ((u32x2 *)out)[i] = o;
+// one thread per (token, 4 columns): slots summed in order 0..topk-1
+__global__ void k_combine(const float *y, const int32_t *pos, int T, int H, int topk,
+                          uint16_t *out) {
+  const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per_t = H / 4;
+  if (q >= (int64_t)T * per_t) return;
+  const int t = (int)(q / per_t), c = (int)(q % per_t) * 4;
+  f32x4 a = {0, 0, 0, 0};
+  for (int j = 0; j < topk; ++j) {
+    const int r = pos[(int64_t)t * topk + j];
+    if (r >= 0) a += *(const f32x4 *)(y + (int64_t)r * H + c);
   }
+  *(u32x2 *)(out + (int64_t)t * H + c) = u32x2{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
 }
 
 }  // namespace
@@ -407,18 +440,24 @@ hipError_t launch_moe(const MoeArgs &p, hipStream_t stream) {
   int32_t *tile_n = (int32_t *)(w + L.tile_n);
   uint8_t *hq = (uint8_t *)(w + L.hq);
   uint8_t *hs = (uint8_t *)(w + L.hs);
-  float *outf = (float *)(w + L.outf);
-  const int64_t TH = (int64_t)p.T * p.H;
+  int32_t *pos = (int32_t *)(w + L.pos);
+  float *y = (float *)(w + L.y);
+  const int64_t TH4 = (int64_t)p.T * (p.H / 4);
 
-  hipLaunchKernelGGL(k_prep, dim3(1024), dim3(256), 0, stream, counts, p.E, outf, TH);
-  hipLaunchKernelGGL(k_count, dim3((L.R + 255) / 256), dim3(256), 0, stream, p.ids, L.R, p.E, counts);
-  hipLaunchKernelGGL(k_place, dim3(p.E), dim3(256), 0, stream, p.ids, L.R, p.E, counts, meta,
-                     sorted, tile_e, tile_r, tile_n);
+  int32_t *offs = (int32_t *)(w + L.offs);
+  const int rb = (L.R + 255) / 256;
+  hipLaunchKernelGGL(k_prep, dim3((p.E + 255) / 256), dim3(256), 0, stream, counts, p.E);
+  hipLaunchKernelGGL(k_count, dim3((L.R + 1023) / 1024), dim3(1024), 0, stream, p.ids, L.R, p.E,
+                     counts, pos);
+  hipLaunchKernelGGL(k_scan, dim3(1), dim3(256), 0, stream, counts, p.E, offs, meta, tile_e,
+                     tile_r, tile_n);
+  hipLaunchKernelGGL(k_scatter, dim3(rb), dim3(256), 0, stream, p.ids, L.R, offs, pos, sorted);
   hipLaunchKernelGGL(k_gateup, dim3(p.I / BNI, L.maxtiles), dim3(256), 0, stream, p, meta, sorted,
                      tile_e, tile_r, tile_n, hq, hs);
   hipLaunchKernelGGL(k_down, dim3((p.H + BNH - 1) / BNH, L.maxtiles), dim3(256), 0, stream, p,
-                     meta, sorted, tile_e, tile_r, tile_n, hq, hs, outf);
-  hipLaunchKernelGGL(k_cast, dim3(1024), dim3(256), 0, stream, outf, p.out, TH);
+                     meta, sorted, tile_e, tile_r, tile_n, hq, hs, y);
+  hipLaunchKernelGGL(k_combine, dim3((unsigned)((TH4 + 255) / 256)), dim3(256), 0, stream, y, pos,
+                     p.T, p.H, p.topk, p.out);
   return hipGetLastError();
 }
 

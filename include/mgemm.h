@@ -174,13 +174,15 @@ int mgemm_w4a4(const void *Aq, const void *As, const float *Sa, const void *Wq,
      h is re-quantised to MXFP8 (E8M0 per 32 along I, OCP MX rule);
      y = h . w2[e]^T;  out[t] = sum_j topk_w[t,j] * y  (FP32), then BF16.
    out: [T,H] BF16.  ws: device workspace of at least
-   mgemm_workspace_bytes(MGEMM_OP_MOE, ...) bytes; its counters are zeroed on
-   `stream` by the call itself before use.  dbg_h: NULL, or a device buffer of
+   mgemm_workspace_bytes(MGEMM_OP_MOE, ...) bytes (routing tables, the
+   re-quantised h rows and the weighted FP32 down-projection rows, T*topk*H*4
+   bytes of the total); it needs no particular contents: the call resets its
+   counters on `stream` before use.  dbg_h: NULL, or a device buffer of
    T*topk*(I + I/32) bytes that receives each (token, slot) row of the
    re-quantised h (I code bytes then I/32 scale bytes) at row t*topk + j.
    H and I must be multiples of 64, topk in [1,16], E in [1,1024], T <= 2^24.
-   The FP32 combine is order-dependent (atomic adds): results agree with the
-   fixed-order sum to FP32 rounding, not bit for bit. */
+   The combine adds each token's slots in order j = 0..topk-1 in FP32 (no
+   atomics): results are run-to-run bit-identical. */
 int mgemm_moe_mxfp8_glu(const void *xq, const void *xs, const int32_t *topk_ids,
                         const float *topk_w, int64_t T, int64_t H, int64_t I,
                         int64_t E, int64_t topk, const void *w13q, const void *w13s,
