@@ -39,8 +39,8 @@ PEAK_VALU_F32 = 78.6
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quick", action="store_true", help="headline kernel only")
     ap.add_argument("--only", default="", help="w4a4|w4a8|bf16|moe (profiling runs)")
@@ -246,7 +246,7 @@ def main():
         wsp = mg.workspace(mg.mgemm_workspace_bytes(mg.OP_MOE, T=T, H=H, I=I, E=E, topk=topk), "moe")
         call = lambda i: mg.mgemm_moe_mxfp8_glu(dm["xq"], dm["xs"], dm["ids"], dm["tw"], dm["w13q"],  # noqa: E731
                                                 dm["w13s"], dm["w2q"], dm["w2s"], o, ws=wsp)
-        ms = timed(torch, call, max(3, args.steps // 2), min(args.warmup, 3), stream)
+        ms = timed(torch, call, max(3, args.steps // 2), min(args.warmup, 10), stream)
         fl = 2.0 * T * topk * (H * 2 * I + I * H)
         tf = fl / (ms * 1e-3) / 1e12
         out["moe"] = {"T": T, "H": H, "I": I, "E": E, "topk": topk, "ms": round(ms, 3),
