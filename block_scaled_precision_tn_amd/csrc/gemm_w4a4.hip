@@ -4,20 +4,22 @@
 //   * both operands' E2M1 codes become E4M3 bytes by the mask-and-shift bit
 //     identity (value x 2^-6), giving FP8 MFMA operands;
 //   * one v_mfma_f32_32x32x16_fp8_fp8 per 16-element group with a zero
-//     accumulator gives the group partial P_g (exact in FP32);
-//   * the two group scales, each decoded and multiplied by 64 (the folded
-//     2^6), form c_g = (64 s_a)(64 s_w) -- exact in FP32; it is produced on the
-//     matrix unit as K = 1 outer products (two 32x32 blocks per instruction),
-//     which keeps the per-element scale products off the vector ALU;
-//   * acc = fma(c_g, P_g, acc) in FP32, groups in ascending K;
-//   * epilogue: acc * (S_a * S_w), BF16 (nearest even) or FP32 store.
+//     accumulator gives the group partial P'_g = 2^-12 P_g (exact in FP32);
+//   * the group scale product c_g = s_a * s_w is formed exactly on the matrix
+//     unit too: a second FP8 MFMA whose operands carry the raw E4M3 scale
+//     bytes at K = 0 and zeros elsewhere (a NaN scale gives a NaN product);
+//   * acc = fma(c_g, P'_g, acc) in FP32, groups in ascending K.  This is the
+//     route's fma((64 s_a)(64 s_w), P'_g, acc) scaled by exactly 2^-12 at
+//     every step, so every rounding is the same;
+//   * epilogue: acc * (4096 S_a S_w), BF16 (nearest even) or FP32 store.
 //
-// Per 32x32 block and group the route costs one FP8 MFMA, half an outer-
-// product MFMA and 16 FMAs; the kernel keeps everything else off those units:
-// codes are converted to E4M3 once, when a stage is written to LDS (not by
-// every wave that reads them), scales are decoded to FP32 then as well, LDS
+// Per 32x32 block and group the route costs two FP8 MFMAs and 16 FP32 FMAs,
+// and the FMAs on the vector ALU are the bound.  Everything else is kept off
+// that unit: codes are converted to E4M3 once, when a stage is written to LDS
+// (not by every wave that reads them), scale bytes go to LDS untouched, LDS
 // holds each (32-row block, group) operand contiguously in lane order (no
-// bank conflicts), and global loads run two stages ahead of their use.
+// bank conflicts), and global loads run two stages ahead of their use with no
+// wait until the stage is written.
 //
 // Workgroup: 512 threads (8 waves, 4x2), tile 128 x 128, wave tile 32 x 64
 // (1 x 2 MFMA blocks of 32 x 32, so 4 waves fit each SIMD).  K is staged
@@ -38,57 +40,57 @@ __device__ __forceinline__ int coff(int row, int g, int h) {
 }
 
 // One stage: each operand's E4M3 codes in MFMA operand order (see coff), and
-// the 4 group scales of each row as FP32 (64 s), group-major.
+// each row's 4 raw group scale bytes, group-major, each widened to 8 bytes so
+// one LDS read yields a whole MFMA operand (the byte at K = 0, zeros above).
 struct Stage {
   uint8_t code[2][BM * GPS * 16];
-  float sc[2][GPS * BM];      // [group][row]
+  uint64_t sc[2][GPS * BM];   // [group][row]: raw E4M3 scale byte, zero-extended to 8 bytes
 };
 
 struct StageRegs {
   u32x4 code;      // 32 codes (groups 2q, 2q+1) of one row (threads < 256: A, else W)
-  uint32_t sc;     // 4 scale bytes of one row (threads < 128: A, < 256: W)
+  uint32_t s0, s1; // scale bytes of groups (0, 1) and (2, 3) of one row, as loaded
 };
 
+// Global loads of one stage.  Every thread issues the same loads with no
+// data-dependent branch or select, so nothing waits for them here: the data
+// is masked when the stage is written to LDS.  (Threads 256..511 repeat the
+// scale loads of threads 0..255; only the latter store them.)
 __device__ __forceinline__ void load_stage(const W4A4Args &p, int m0, int n0, int g0, int G,
                                            int tid, StageRegs &r) {
   const int64_t rowb = p.K / 2, rows = p.K / 16;
-  const int row = (tid & 255) >> 1, q = tid & 1;
   {
+    const int row = (tid & 255) >> 1, q = tid & 1;
     const int op = tid >> 8;
     const uint8_t *base = op == 0 ? p.aq : p.wq;
     const int R = op == 0 ? p.M : p.N, o = op == 0 ? m0 : n0;
     const int g = g0 + 2 * q;               // G is even (K % 32 == 0): g < G covers g + 1
     int grow = o + row;
     grow = grow < R ? grow : R - 1;
-    const int gs = g < G ? g : G - 2;       // in-bounds address; data masked below
-    const u32x4 v = *(const u32x4 *)(base + (int64_t)grow * rowb + (int64_t)gs * 8);
-    r.code = g < G ? v : u32x4{0, 0, 0, 0};
+    const int gs = g < G ? g : G - 2;       // in-bounds address
+    r.code = *(const u32x4 *)(base + (int64_t)grow * rowb + (int64_t)gs * 8);
   }
-  if (tid < 256) {
-    const int op = tid >> 7, srow = tid & 127;
+  {
+    const int op = (tid >> 7) & 1, srow = tid & 127;
     const uint8_t *base = op == 0 ? p.as : p.ws;
     const int R = op == 0 ? p.M : p.N, o = op == 0 ? m0 : n0;
     int grow = o + srow;
     grow = grow < R ? grow : R - 1;
     const uint16_t *s16 = (const uint16_t *)(base + (int64_t)grow * rows);
-    uint32_t w = 0;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int g = g0 + 2 * j;
-      const uint32_t v = s16[(g < G ? g : G - 2) >> 1];
-      w |= (g < G ? v : 0u) << (16 * j);
-    }
-    r.sc = w;
+    r.s0 = s16[(g0 < G ? g0 : G - 2) >> 1];
+    r.s1 = s16[(g0 + 2 < G ? g0 + 2 : G - 2) >> 1];
   }
 }
 
-__device__ __forceinline__ void store_stage(Stage &s, int tid, const StageRegs &r) {
-  const int row = (tid & 255) >> 1, q = tid & 1;
+// Stage g0 to LDS: codes converted to E4M3, groups at or past G zeroed.
+__device__ __forceinline__ void store_stage(Stage &s, int tid, const StageRegs &r, int g0, int G) {
   {
+    const int row = (tid & 255) >> 1, q = tid & 1;
     const int op = tid >> 8;
+    const u32x4 v = g0 + 2 * q < G ? r.code : u32x4{0, 0, 0, 0};
     // dwords: (group 2q, half 0) (2q, 1) (2q+1, 0) (2q+1, 1)
-    const uint64_t e0 = nvfp4x8_to_e4m3x8(r.code[0]), e1 = nvfp4x8_to_e4m3x8(r.code[1]);
-    const uint64_t e2 = nvfp4x8_to_e4m3x8(r.code[2]), e3 = nvfp4x8_to_e4m3x8(r.code[3]);
+    const uint64_t e0 = nvfp4x8_to_e4m3x8(v[0]), e1 = nvfp4x8_to_e4m3x8(v[1]);
+    const uint64_t e2 = nvfp4x8_to_e4m3x8(v[2]), e3 = nvfp4x8_to_e4m3x8(v[3]);
     uint8_t *c = s.code[op];
     *(uint64_t *)(c + coff(row, 2 * q, 0)) = e0;
     *(uint64_t *)(c + coff(row, 2 * q, 1)) = e1;
@@ -96,14 +98,15 @@ __device__ __forceinline__ void store_stage(Stage &s, int tid, const StageRegs &
     *(uint64_t *)(c + coff(row, 2 * q + 1, 1)) = e3;
   }
   if (tid < 256) {
-    const int op = tid >> 7, srow = tid & 127;
+    const uint32_t w = (g0 < G ? r.s0 : 0u) | ((g0 + 2 < G ? r.s1 : 0u) << 16);
 #pragma unroll
-    for (int g = 0; g < GPS; ++g) s.sc[op][g * BM + srow] = e4m3_x64_to_f32_nan((r.sc >> (8 * g)) & 0xFFu);
+    for (int g = 0; g < GPS; ++g) s.sc[tid >> 7][g * BM + (tid & 127)] = (w >> (8 * g)) & 0xFFu;
   }
 }
 
 __global__ __launch_bounds__(512, 2) void w4a4_fp8route_kernel(W4A4Args p) {
   __shared__ __attribute__((aligned(16))) Stage lds[2];
+  __shared__ uint64_t zsc[GPS * BM];   // zeros: the A-side scale operand of lanes h = 1
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, h = lane >> 5;
@@ -122,42 +125,47 @@ __global__ __launch_bounds__(512, 2) void w4a4_fp8route_kernel(W4A4Args p) {
     const uint8_t *pa = cur.code[0] + coff(wm * 32, 0, 0) + 8 * lane;
     const uint8_t *pw0 = cur.code[1] + coff(wn * 64, 0, 0) + 8 * lane;
     const uint8_t *pw1 = cur.code[1] + coff(wn * 64 + 32, 0, 0) + 8 * lane;
-    const float *psa = cur.sc[0] + wm * 32 + l32;
-    // lanes 0..31 carry column block 0's scales, lanes 32..63 column block 1's
-    const float *psw = cur.sc[1] + wn * 64 + lane;
+    // scale operands: lane (row, h = 0) holds its row's scale byte at K = 0 and
+    // zeros elsewhere; on the A side lanes h = 1 read zeros, so the K = 16
+    // product is exactly s_a * s_w (a NaN scale still yields NaN)
+    const uint64_t *psa = (h ? zsc : cur.sc[0]) + wm * 32 + l32;
+    const uint64_t *psw = cur.sc[1] + wn * 64 + l32;
 #pragma unroll 1
     for (int g = 0; g < GPS; ++g) {
       const uint64_t a = *(const uint64_t *)(pa + 512 * g);
       const uint64_t w0 = *(const uint64_t *)(pw0 + 512 * g), w1 = *(const uint64_t *)(pw1 + 512 * g);
-      const f32x32 c = mfma_outer2(psa[BM * g], psw[BM * g]);
+      const uint64_t sa = psa[BM * g], sw0 = psw[BM * g], sw1 = psw[BM * g + 32];
+      const f32x16 c0 = mfma_fp8(sa, sw0, zero);
+      const f32x16 c1 = mfma_fp8(sa, sw1, zero);
       const f32x16 p0 = mfma_fp8(a, w0, zero);
       const f32x16 p1 = mfma_fp8(a, w1, zero);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[0][r] = __builtin_fmaf(c[r], p0[r], acc[0][r]);
+      for (int r = 0; r < 16; ++r) acc[0][r] = __builtin_fmaf(c0[r], p0[r], acc[0][r]);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[1][r] = __builtin_fmaf(c[16 + r], p1[r], acc[1][r]);
+      for (int r = 0; r < 16; ++r) acc[1][r] = __builtin_fmaf(c1[r], p1[r], acc[1][r]);
     }
   };
+  for (int i = tid; i < GPS * BM; i += 512) zsc[i] = 0;
   StageRegs r0, r1;
   load_stage(p, m0, n0, 0, G, tid, r0);
   load_stage(p, m0, n0, GPS, G, tid, r1);
-  store_stage(lds[0], tid, r0);
+  store_stage(lds[0], tid, r0, 0, G);
   __syncthreads();
   load_stage(p, m0, n0, 2 * GPS, G, tid, r0);
   for (int s = 0; s < S; s += 2) {
     // lds[0] holds stage s, r1 stage s+1, r0 stage s+2 (in flight)
     compute(lds[0]);
-    store_stage(lds[1], tid, r1);
+    store_stage(lds[1], tid, r1, (s + 1) * GPS, G);
     __syncthreads();
     load_stage(p, m0, n0, (s + 3) * GPS, G, tid, r1);
     if (s + 1 >= S) break;
     compute(lds[1]);
-    store_stage(lds[0], tid, r0);
+    store_stage(lds[0], tid, r0, (s + 2) * GPS, G);
     __syncthreads();
     load_stage(p, m0, n0, (s + 4) * GPS, G, tid, r0);
   }
 
-  const float gs = *p.Sa * *p.Sw;
+  const float gs = *p.Sa * *p.Sw * 4096.0f;  // c_g lacks the folded 2^6 * 2^6
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int col = n0 + wn * 64 + j * 32 + l32;
