@@ -101,14 +101,6 @@ __device__ __forceinline__ float e4m3_x64_to_f32_nan(uint32_t b) {
   return (b & 0x7Fu) == 0x7Fu ? __builtin_nanf("") : v;
 }
 
-// Two 32x32 outer products of K = 1 in FP32 (v_mfma_f32_32x32x1_2b_f32):
-// output registers 16b..16b+15 hold block b, laid out as any 32x32 MFMA
-// result, with block b's (row i, column j) = a[lane 32b+i] * b[lane 32b+j].
-__device__ __forceinline__ f32x32 mfma_outer2(float a, float b) {
-  const f32x32 z = {0};
-  return __builtin_amdgcn_mfma_f32_32x32x1f32(a, b, z, 0, 0, 0);
-}
-
 // FP32 -> BF16 bits, round to nearest even (NaN stays NaN)
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   uint32_t u = __builtin_bit_cast(uint32_t, f);
@@ -135,6 +127,22 @@ __device__ __forceinline__ void xcd_tile(int id, int tiles_m, int tiles_n, int &
   const int gsz = tiles_m - first < GROUP ? tiles_m - first : GROUP;
   tm = first + (t % per_group) % gsz;
   tn = (t % per_group) / gsz;
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14; expcnt (6:4) and lgkmcnt (11:8) at maximum).
+// A workgroup barrier written as __syncthreads() carries a memory fence that
+// waits for every outstanding global load; kernels that keep loads in flight
+// across a barrier use these waits with __builtin_amdgcn_s_barrier() instead.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// s_waitcnt lgkmcnt(0) only
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt(63 | (3 << 14) | (7 << 4) | (0 << 8));
 }
 
 // row held by accumulator register r of lane l (see the layout note above)

@@ -43,19 +43,6 @@ __device__ __forceinline__ int swz(int row, int chunk) {
   return row * ROWB + ((chunk ^ ((row >> 1) & 7)) << 4);
 }
 
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
-// vmcnt in bits 3:0 and 15:14; expcnt (6:4) and lgkmcnt (11:8) at maximum)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// s_waitcnt lgkmcnt(0) only
-__device__ __forceinline__ void wait_lgkm0() {
-  __builtin_amdgcn_s_waitcnt(63 | (3 << 14) | (7 << 4) | (0 << 8));
-}
-
 // E2M1 code (low 4 bits) -> FP32 value
 __device__ __forceinline__ float e2m1_to_f32(uint32_t c) {
   const uint32_t mag = c & 7u;

@@ -18,13 +18,17 @@
 //     its 32-row slab from LDS.  Code rows are XOR-swizzled in 16-byte chunks
 //     so the 32 rows one operand read touches spread over the LDS banks;
 //     token rows are padded by 8 bytes for the same reason.
-//   * K is cut into 256-element ranges, four per workgroup; all four are
-//     requested at once (register buffers), so the whole weight stream is in
-//     flight from the start, and each range is staged and computed as it
-//     lands -- the work left after the last bytes arrive is one short range.
+//   * K is cut into 256-element ranges, two per workgroup (K = 14336 gives
+//     28 splits and 1176 workgroups for N = 5376); both are requested at once
+//     (register buffers), so the whole weight stream is in flight from the
+//     start, and each range is staged and computed as soon as its own loads
+//     land -- the work left after the last bytes arrive is one short range.
 //   * the K ranges of a weight tile are split over ks workgroups (split-K);
 //     each writes an FP32 partial, and a second kernel sums the partials in
-//     split order 0..ks-1 -- results are bit-identical run to run.
+//     split order 0..ks-1 -- results are bit-identical run to run.  (A split
+//     that reduces in place needs its partials visible across the XCDs'
+//     separate L2 caches within the kernel, which costs more than the second
+//     launch.)
 // Tokens sit on the MFMA's A side, padded to 32: lanes of token rows >= M
 // read row 0 (those MFMA rows are never stored), and only the accumulator
 // registers that hold real tokens are scaled.  M > 32 runs in slices of 32.
@@ -36,7 +40,7 @@ namespace {
 
 constexpr int NT = 128;       // weight rows per workgroup (4 waves x 32)
 constexpr int KR = 256;       // K-elements per range
-constexpr int RPW = 4;        // ranges per workgroup, all requested at once
+constexpr int RPW = 2;        // ranges per workgroup, all requested at once
 constexpr int MS = 32;        // tokens per launch
 
 constexpr int ROWB = KR / 2;          // code bytes per weight row per range
@@ -68,12 +72,20 @@ __device__ __forceinline__ int woff(int row, int chunk) {
 template <int MT>
 struct RangeRegs {
   static constexpr int ACH = (MT * (KR / 16) + 255) / 256;  // token chunks per thread
+  // global loads range_load issues per thread (its scale loads: one 8-byte
+  // load when K % 256 == 0, else four 2-byte loads)
+  template <bool SFAST>
+  static constexpr int loads() { return WCH + (SFAST ? 1 : 4) + ACH; }
   u32x4 w[WCH];
-  u32x2 s;         // 8 scale bytes: row tid / 2, groups 8 (tid % 2) .. +7
+  uint32_t s[4];   // scale bytes of row tid / 2, groups 8 (tid % 2) .. +7: two
+                   // dwords (K % 256 == 0) or four 2-byte pairs, as loaded
   u32x4 a[ACH];
 };
 
-// loads of K range [k0, k0 + klen) of this workgroup's weight tile and tokens
+// Loads of K range [k0, k0 + klen) of this workgroup's weight tile and
+// tokens.  Addresses are clamped in bounds and nothing is selected on the
+// loaded data here -- a use of it would make the loads wait at once; the
+// data past klen (or past the last token) is masked in range_store.
 template <int MT, bool SFAST>
 __device__ __forceinline__ void range_load(const W4A8Args &p, int n0, int k0, int klen, int tid,
                                            RangeRegs<MT> &r) {
@@ -84,28 +96,24 @@ __device__ __forceinline__ void range_load(const W4A8Args &p, int n0, int k0, in
     const int c = tid + 256 * i, row = c / CHUNKS, ch = c % CHUNKS;
     const int n = n0 + row < p.N ? n0 + row : p.N - 1;
     const bool in = ch * 32 < klen;
-    const u32x4 v = *(const u32x4 *)(p.wq + (int64_t)n * (p.K / 2) + k0 / 2 + (in ? ch : 0) * 16);
-    r.w[i] = in ? v : u32x4{0, 0, 0, 0};
+    r.w[i] = *(const u32x4 *)(p.wq + (int64_t)n * (p.K / 2) + k0 / 2 + (in ? ch : 0) * 16);
   }
   {
     static_assert(SB == 16, "one scale row per thread pair");
     const int row = tid >> 1, q = tid & 1;
     const int n = n0 + row < p.N ? n0 + row : p.N - 1;
-    const bool in = 128 * q < klen;              // groups 8q.. of this range exist
     const uint8_t *srow = p.ws + (int64_t)n * G + k0 / 16;
     if constexpr (SFAST) {  // K % 256 == 0: 8-byte aligned scale runs
+      const bool in = 128 * q < klen;            // groups 8q.. of this range exist
       const u32x2 x = *(const u32x2 *)(srow + (in ? 8 * q : 0));
-      r.s = in ? x : u32x2{0, 0};
+      r.s[0] = x[0];
+      r.s[1] = x[1];
     } else {                // K % 32 == 0: 2-byte aligned, loaded in pairs
-      uint32_t b[2] = {0, 0};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int g = 8 * q + 2 * e;             // within the range
-        const bool ok = 16 * g < klen;
-        const uint32_t v = *(const uint16_t *)(srow + (ok ? g : 0));
-        b[e >> 1] |= (ok ? v : 0u) << (16 * (e & 1));
+        r.s[e] = *(const uint16_t *)(srow + (16 * g < klen ? g : 0));
       }
-      r.s = u32x2{b[0], b[1]};
     }
   }
 #pragma unroll
@@ -113,26 +121,38 @@ __device__ __forceinline__ void range_load(const W4A8Args &p, int n0, int k0, in
     const int c = tid + 256 * i, t = c / (KR / 16), ch = c % (KR / 16);
     const bool in = t < p.M && ch * 16 < klen;
     const int tt = t < p.M ? t : p.M - 1;
-    const u32x4 x = *(const u32x4 *)(p.aq + (int64_t)tt * p.K + k0 + (in ? ch : 0) * 16);
-    r.a[i] = in ? x : u32x4{0, 0, 0, 0};
+    r.a[i] = *(const u32x4 *)(p.aq + (int64_t)tt * p.K + k0 + (in ? ch : 0) * 16);
   }
 }
 
-template <int MT>
-__device__ __forceinline__ void range_store(Tile<MT> &tile, int M, int tid, const RangeRegs<MT> &r) {
+template <int MT, bool SFAST>
+__device__ __forceinline__ void range_store(Tile<MT> &tile, int M, int klen, int tid,
+                                            const RangeRegs<MT> &r) {
   constexpr int ACH = RangeRegs<MT>::ACH;
 #pragma unroll
   for (int i = 0; i < WCH; ++i) {
     const int c = tid + 256 * i, row = c / CHUNKS, ch = c % CHUNKS;
-    const u32x4 v = r.w[i];
+    const u32x4 v = ch * 32 < klen ? r.w[i] : u32x4{0, 0, 0, 0};
     *(u32x4 *)(tile.w + woff(row, ch)) = u32x4{v[0], v[2], v[1], v[3]};
   }
   {
     const int row = tid >> 1, q = tid & 1;
+    uint32_t sw[2];
+    if constexpr (SFAST) {
+      const bool in = 128 * q < klen;
+      sw[0] = in ? r.s[0] : 0u;
+      sw[1] = in ? r.s[1] : 0u;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const bool in0 = 16 * (8 * q + 4 * e) < klen, in1 = 16 * (8 * q + 4 * e + 2) < klen;
+        sw[e] = (in0 ? r.s[2 * e] : 0u) | ((in1 ? r.s[2 * e + 1] : 0u) << 16);
+      }
+    }
     float *dst = tile.s + row * SROWF + 8 * q;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t w = r.s[j >> 1] >> (16 * (j & 1));
+      const uint32_t w = sw[j >> 1] >> (16 * (j & 1));
       *(f32x2 *)(dst + 2 * j) = f32x2{e4m3_x64_to_f32_nan(w & 0xFFu), e4m3_x64_to_f32_nan((w >> 8) & 0xFFu)};
     }
   }
@@ -144,8 +164,9 @@ __device__ __forceinline__ void range_store(Tile<MT> &tile, int M, int tid, cons
     // each 8-byte slice in even/odd byte order (the converted weight codes
     // come out in that order); the slices of groups 2c and 2c+1 that one
     // MFMA K-half reads are placed side by side: [lo(2c) lo(2c+1) | hi(2c) hi(2c+1)]
-    const uint64_t lo = e4m3x8_even_odd((uint64_t)r.a[i][0] | ((uint64_t)r.a[i][1] << 32));
-    const uint64_t hi = e4m3x8_even_odd((uint64_t)r.a[i][2] | ((uint64_t)r.a[i][3] << 32));
+    const u32x4 av = t < M && 16 * g < klen ? r.a[i] : u32x4{0, 0, 0, 0};
+    const uint64_t lo = e4m3x8_even_odd((uint64_t)av[0] | ((uint64_t)av[1] << 32));
+    const uint64_t hi = e4m3x8_even_odd((uint64_t)av[2] | ((uint64_t)av[3] << 32));
     uint8_t *dst = tile.a + t * AROW + 32 * (g >> 1) + 8 * (g & 1);
     *(uint64_t *)dst = lo;
     *(uint64_t *)(dst + 16) = hi;
@@ -199,6 +220,18 @@ __device__ __forceinline__ void compute_any(const Tile<Acc<QUADS>::MT> &tile, in
     compute_range<QUADS, false>(tile, row, trow, h, klen / 32, acc);
 }
 
+// wait until at most `left` ranges' loads (LPR per range) are still in flight
+template <int LPR>
+__device__ __forceinline__ void wait_ranges_left(int left) {
+  static_assert(RPW <= 4 && (RPW - 1) * LPR < 64, "vmcnt range");
+  switch (left) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<LPR>(); break;
+    case 2: wait_vmcnt<2 * LPR>(); break;
+    default: wait_vmcnt<3 * LPR>(); break;
+  }
+}
+
 template <int QUADS, bool SFAST>
 __global__ __launch_bounds__(256) void w4a8_decode_kernel(W4A8Args p, int ks, float *part) {
   constexpr int MT = Acc<QUADS>::MT;
@@ -216,29 +249,41 @@ __global__ __launch_bounds__(256) void w4a8_decode_kernel(W4A8Args p, int ks, fl
 
   // All of the workgroup's ranges (at most RPW) are requested at once into
   // register buffers, so the whole weight stream is in flight from the start;
-  // each range is then staged through the one LDS tile and computed as it
-  // lands (loads complete in issue order).  A range past the run is requested
-  // with length 0: all of its data is masked and only each row's first chunk
-  // is touched.
+  // each range is then staged through the one LDS tile and computed as soon as
+  // its own loads have landed (loads complete in issue order, so range j waits
+  // only for its batch), while the later ranges are still arriving.  A range
+  // past the run is requested with length 0: its data is masked and only each
+  // row's first chunk is touched.
   auto klen = [&](int rg) {
     return rg >= rend ? 0 : (p.K - rg * KR < KR ? p.K - rg * KR : KR);
   };
   auto kstart = [&](int rg) { return (rg < rend ? rg : rend - 1) * KR; };
+  constexpr int LPR = RangeRegs<MT>::template loads<SFAST>();
   RangeRegs<MT> rr[RPW];
 #pragma unroll
-  for (int j = 0; j < RPW; ++j) range_load<MT, SFAST>(p, n0, kstart(rbeg + j), klen(rbeg + j), tid, rr[j]);
+  for (int j = 0; j < RPW; ++j) {
+    range_load<MT, SFAST>(p, n0, kstart(rbeg + j), klen(rbeg + j), tid, rr[j]);
+    __builtin_amdgcn_sched_barrier(0);  // ranges are issued in order
+  }
+  // (Every range, even an empty one, is stored and computed with no branch
+  // around it: a load whose only use sits in a branch is moved into it, and
+  // the waits before it then cover every load in flight.)
 #pragma unroll
   for (int j = 0; j < RPW; ++j) {
-    if (rbeg + j >= rend) break;
-    if (j > 0) __syncthreads();
-    range_store(tile, p.M, tid, rr[j]);
-    __syncthreads();
+    if (j > 0) {  // every wave is done reading the previous range
+      wait_lgkm0();
+      __builtin_amdgcn_s_barrier();
+    }
+    wait_ranges_left<LPR>(RPW - 1 - j);
+    range_store<MT, SFAST>(tile, p.M, klen(rbeg + j), tid, rr[j]);
+    wait_lgkm0();
+    __builtin_amdgcn_s_barrier();
     compute_any<QUADS>(tile, row, trow, h, klen(rbeg + j), acc);
   }
 
   const int n = n0 + row;
-  if (n >= p.N) return;
   if (ks == 1) {
+    if (n >= p.N) return;
     const float sw = *p.Sw;
 #pragma unroll
     for (int r = 0; r < Acc<QUADS>::NREG; ++r) {
@@ -252,29 +297,34 @@ __global__ __launch_bounds__(256) void w4a8_decode_kernel(W4A8Args p, int ks, fl
     }
     return;
   }
+
+  if (n < p.N) {
 #pragma unroll
-  for (int r = 0; r < Acc<QUADS>::NREG; ++r) {
-    const int t = acc_row(r, lane);
-    if (t < p.M) part[((int64_t)kc * p.M + t) * p.N + n] = acc[r];
+    for (int r = 0; r < Acc<QUADS>::NREG; ++r) {
+      const int t = acc_row(r, lane);
+      if (t < p.M) part[((int64_t)kc * p.M + t) * p.N + n] = acc[r];
+    }
   }
 }
 
-// C[t,n] = (sum over splits s = 0..ks-1, in order, of part[s,t,n]) * a_tok[t] * S_w
+// C[t,n] = (sum over splits s = 0..ks-1, in order, of part[s,t,n]) * a_tok[t] * S_w.
+// Partials are requested CH at a time (all of them when ks <= CH, so a
+// decode-sized reduction waits on one memory latency).
 __global__ __launch_bounds__(64) void w4a8_splitk_reduce(W4A8Args p, int ks, const float *part) {
+  constexpr int CH = 16;
   const int64_t i = (int64_t)blockIdx.x * 64 + threadIdx.x;
   const int64_t mn = (int64_t)p.M * p.N;
   if (i >= mn) return;
   const int t = (int)(i / p.N);
   float v = 0.0f;
-  int s = 0;
-  for (; s + 8 <= ks; s += 8) {  // eight independent loads in flight, summed in order
-    float x[8];
+  for (int s0 = 0; s0 < ks; s0 += CH) {
+    float x[CH];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] = part[(int64_t)(s + j) * mn + i];
+    for (int j = 0; j < CH; ++j) x[j] = part[(int64_t)(s0 + j < ks ? s0 + j : s0) * mn + i];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v += x[j];
+    for (int j = 0; j < CH; ++j)
+      if (s0 + j < ks) v += x[j];
   }
-  for (; s < ks; ++s) v += part[(int64_t)s * mn + i];
   v *= p.atok[t] * *p.Sw;
   if (p.out_f32)
     ((float *)p.C)[i] = v;
@@ -306,13 +356,13 @@ int64_t w4a8_max_n() { return (int64_t)1 << 30; }
 
 hipError_t launch_w4a8(const W4A8Args &p0, hipStream_t stream) {
   const int ks = splits(p0.K);
+  float *part = ks > 1 ? (float *)p0.work : nullptr;
   for (int m0 = 0; m0 < p0.M; m0 += MS) {
     W4A8Args p = p0;
     p.M = p0.M - m0 < MS ? p0.M - m0 : MS;
     p.aq = p0.aq + (int64_t)m0 * p0.K;
     p.atok = p0.atok + m0;
     p.C = (char *)p0.C + (int64_t)m0 * p0.N * (p0.out_f32 ? 4 : 2);
-    float *part = ks > 1 ? (float *)p0.work : nullptr;
     if (p.M > 24) launch_one<4>(p, ks, part, stream);
     else if (p.M > 16) launch_one<3>(p, ks, part, stream);
     else if (p.M > 8) launch_one<2>(p, ks, part, stream);

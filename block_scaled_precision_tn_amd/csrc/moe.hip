@@ -172,12 +172,6 @@ __device__ __forceinline__ int mx_off(int row, int chunk) {
   return row * BK + ((chunk ^ ((row >> 2) & 3)) << 4);
 }
 
-template <int N>
-__device__ __forceinline__ void mx_wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
 struct MxRows {
   const uint8_t *a[2], *b[2];   // code rows this lane loads: rows 16 (2 wave + j) + lane / 4
   const uint8_t *s;             // scale row of row (64 wave + lane) % 128 (A if < 128, else B)
@@ -214,7 +208,7 @@ __device__ __forceinline__ void mx_mainloop(const MxRows &rows, int Ktot, const 
     __builtin_amdgcn_sched_barrier(0);
     // stage s has landed once at most stage s+1's loads are outstanding; the
     // bare s_barrier (a fenced one would wait for every load in flight)
-    mx_wait_vmcnt<LOADS>();
+    wait_vmcnt<LOADS>();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     // stage s+2 into the slot stage s-1 used (every wave is past it); stages
@@ -255,7 +249,7 @@ __device__ __forceinline__ void mx_mainloop(const MxRows &rows, int Ktot, const 
   }
   if (S % 3 >= 1) step(full, a0, b0, s0, a2, b2, s2);
   if (S % 3 == 2) step(full + 1, a1, b1, s1, a0, b0, s0);
-  mx_wait_vmcnt<0>();
+  wait_vmcnt<0>();
   // the slots are reused by the next tile only after this barrier
   __builtin_amdgcn_s_barrier();
 }

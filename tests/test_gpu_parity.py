@@ -206,6 +206,28 @@ def test_sign_and_scale_invariants():
         assert np.array_equal(c2[:, 7], 2 * c0[:, 7])
 
 
+def test_nan_scale_propagates():
+    """An E4M3 NaN scale byte (0x7F or 0xFF) makes every output that reads its
+    group NaN, as in the oracle's decode; all other outputs are unchanged
+    bit for bit (W4A4, FP32 output)."""
+    from gpu_cases import GPU, oracle_full
+    inp = synth.w4a4(64, 96, 256, seed=41)
+    c0 = GPU["w4a4"](inp, True)
+    as_ = inp["as_"].copy()
+    as_[3, 5] = 0x7F
+    ws = inp["ws"].copy()
+    ws[10, 2] = 0xFF
+    bad = dict(inp, as_=as_, ws=ws)
+    c1 = GPU["w4a4"](bad, True)
+    nan = np.zeros(c1.shape, bool)
+    nan[3, :] = True
+    nan[:, 10] = True
+    c64, _ = oracle_full("w4a4", bad)
+    assert np.array_equal(np.isnan(c64), nan)
+    assert np.array_equal(np.isnan(c1), nan)
+    assert np.array_equal(c1[~nan], c0[~nan])
+
+
 # ------------------------------------------------------------------- plan
 def test_plan_on_device():
     import block_scaled_precision_tn_amd as mg
