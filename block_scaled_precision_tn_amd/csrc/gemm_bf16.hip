@@ -182,18 +182,25 @@ __global__ __launch_bounds__(NTHR, 1) void bf16_gemm_kernel(Bf16Args p) {
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     issue(s + 2, na, nw);
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      u32x4 fa[2], fw[2];
+    // operand fragments double-buffered: the reads of K-step kk+1 are in
+    // flight while the MFMAs of step kk run
+    u32x4 fa[2][2], fw[2][2];
+    auto frag = [&](int kk, int b) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        fa[i] = *(const u32x4 *)(la + swz(wm * 64 + i * 32 + l32, 2 * kk + h));
-        fw[i] = *(const u32x4 *)(lw + swz(wn * 64 + i * 32 + l32, 2 * kk + h));
+        fa[b][i] = *(const u32x4 *)(la + swz(wm * 64 + i * 32 + l32, 2 * kk + h));
+        fw[b][i] = *(const u32x4 *)(lw + swz(wn * 64 + i * 32 + l32, 2 * kk + h));
       }
+    };
+    frag(0, 0);
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      if (kk + 1 < BK / 16) frag(kk + 1, (kk + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);  // keep those reads ahead of the MFMAs
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma_bf16(fa[i], fw[j], acc[i][j]);
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma_bf16(fa[kk & 1][i], fw[kk & 1][j], acc[i][j]);
     }
   };
   if (WQ) wq_load(p, n0, 0, tid, wr);
