@@ -156,15 +156,17 @@ __global__ void k_scatter(const int32_t *ids, int R, const int32_t *offs, int32_
 // of an instruction lands at its LDS base + i * size), three stages of 64 K
 // deep, so two stages are in flight while one is computed.  Per stage and
 // operand a 128 x 64-byte code tile, rows XOR-swizzled in 16-byte chunks (see
-// mx_off) so MFMA fragment reads hit distinct banks, and the rows' two E8M0
-// scale bytes (A rows, then B rows; a 2-byte direct load fills one LDS dword
-// per lane, low half).  A rows are gathered: every lane holds the global row
-// pointers of the rows it loads.
+// mx_off) so MFMA fragment reads hit distinct banks; the rows' E8M0 scale
+// bytes (A rows, then B rows) arrive 8 stages at a time when K % 512 == 0,
+// else per stage (see mx_issue_sc16 / mx_issue_sc2).  A rows are gathered:
+// every lane holds the global row pointers of the rows it loads.
 typedef __attribute__((address_space(1))) void gvoid;
 typedef __attribute__((address_space(3))) void lvoid;
 
 constexpr int MX_CODE = BM * BK;          // bytes of one operand's codes per stage
-constexpr int MX_SC = 2 * BM * 4;         // scale dwords per stage (A rows then B rows)
+constexpr int SCH = 8;                    // stages per scale chunk (K % 512 == 0)
+constexpr int MX_SCC = 2 * BM * 2 * SCH;  // scale bytes per chunk: 16 per row (A rows then B rows)
+constexpr int MX_SCS = 2 * BM * 4;        // scale bytes per stage otherwise: one dword per row
 
 // chunk `chunk` (16 bytes) of 64-byte row `row`: XOR-ed with (row / 4) % 4,
 // so 16 consecutive rows at one chunk index cover all 64 LDS banks
@@ -177,9 +179,9 @@ struct MxRows {
   const uint8_t *s;             // scale row of row (64 wave + lane) % 128 (A if < 128, else B)
 };
 
-// lane's loads of one stage at k0: 2 A + 2 B code chunks, 1 scale pair
-__device__ __forceinline__ void mx_issue(const MxRows &r, int k0, uint8_t *la, uint8_t *lb,
-                                         uint8_t *ls, int wave, int lane) {
+// lane's loads of one stage at k0: 2 A + 2 B code chunks
+__device__ __forceinline__ void mx_issue(const MxRows &r, int k0, uint8_t *la, uint8_t *lb, int wave,
+                                         int lane) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int blk = 2 * wave + j, row = 16 * blk + (lane >> 2), slot = lane & 3;
@@ -187,33 +189,67 @@ __device__ __forceinline__ void mx_issue(const MxRows &r, int k0, uint8_t *la, u
     __builtin_amdgcn_global_load_lds((gvoid *)(r.a[j] + k0 + 16 * chunk), (lvoid *)(la + 1024 * blk), 16, 0, 0);
     __builtin_amdgcn_global_load_lds((gvoid *)(r.b[j] + k0 + 16 * chunk), (lvoid *)(lb + 1024 * blk), 16, 0, 0);
   }
+}
+
+// Scale bytes.  When the scale rows are a multiple of 16 bytes long (K % 512
+// == 0), a lane loads its row's 16 bytes for 8 stages at once (chunk c:
+// stages 8c .. 8c+7), landing at ls + 16 * (64 wave + lane); otherwise it
+// loads the 2 bytes of one stage, landing in one dword per lane (low half) at
+// ls + 4 * (64 wave + lane).  Each such load touches one row per lane, and
+// the texture path's cost grows with the rows an instruction touches.
+__device__ __forceinline__ void mx_issue_sc16(const MxRows &r, int c, uint8_t *ls, int wave) {
+  __builtin_amdgcn_global_load_lds((gvoid *)(r.s + 16 * c), (lvoid *)(ls + 1024 * wave), 16, 0, 0);
+}
+__device__ __forceinline__ void mx_issue_sc2(const MxRows &r, int k0, uint8_t *ls, int wave) {
   __builtin_amdgcn_global_load_lds((gvoid *)(r.s + k0 / 32), (lvoid *)(ls + 256 * wave), 2, 0, 0);
 }
 
-template <int NB>
+template <int NB, bool SC16>
 __device__ __forceinline__ void mx_mainloop(const MxRows &rows, int Ktot, const int bsel[NB],
                                             f32x16 (&acc)[2][NB]) {
   // three ring slots as separate arrays: the compiler can tell loads landing
-  // in one slot from reads of another
+  // in one slot from reads of another.  Scales: two chunk buffers (SC16) or a
+  // slot per code slot.
+  constexpr int SC_BYTES = SC16 ? MX_SCC : MX_SCS;
   __shared__ __attribute__((aligned(1024))) uint8_t a0[MX_CODE], a1[MX_CODE], a2[MX_CODE];
   __shared__ __attribute__((aligned(1024))) uint8_t b0[MX_CODE], b1[MX_CODE], b2[MX_CODE];
-  __shared__ __attribute__((aligned(256))) uint8_t s0[MX_SC], s1[MX_SC], s2[MX_SC];
+  __shared__ __attribute__((aligned(1024))) uint8_t c0[SC_BYTES], c1[SC_BYTES], c2[SC16 ? 16 : SC_BYTES];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, h = lane >> 5, l32 = lane & 31;
   const int S = Ktot / BK;
-  constexpr int LOADS = 5;   // DMA instructions per lane per stage
+  // direct loads per lane per stage: 4 code chunks (+ the scale pair when
+  // not SC16; a scale chunk is issued before the code loads of its first
+  // stage, so waiting for a stage's code loads covers it)
+  constexpr int LOADS = SC16 ? 4 : 5;
 
-  auto step = [&](int s, const uint8_t *la, const uint8_t *lb, const uint8_t *ls,
-                  uint8_t *na, uint8_t *nb, uint8_t *ns) {
+  // one stage: stage s sits in (la, lb[, lc]); stage s+2 is issued into
+  // (na, nb[, nc]), the slot stage s-1 used
+  auto step = [&](int s, const uint8_t *la, const uint8_t *lb, const uint8_t *lc, uint8_t *na,
+                  uint8_t *nb, uint8_t *nc) {
     __builtin_amdgcn_sched_barrier(0);
     // stage s has landed once at most stage s+1's loads are outstanding; the
     // bare s_barrier (a fenced one would wait for every load in flight)
     wait_vmcnt<LOADS>();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    // stage s+2 into the slot stage s-1 used (every wave is past it); stages
-    // past the end reload the last one (never computed)
-    mx_issue(rows, (s + 2 < S ? s + 2 : S - 1) * BK, na, nb, ns, wave, lane);
+    // stages past the end reload the last one (never computed); a new scale
+    // chunk goes to the buffer whose stages every wave has finished
+    const int t = s + 2 < S ? s + 2 : S - 1;
+    if constexpr (SC16) {
+      if ((s + 2) % SCH == 0 && s + 2 < S) mx_issue_sc16(rows, (s + 2) / SCH, ((s + 2) / SCH) & 1 ? c1 : c0, wave);
+    } else {
+      mx_issue_sc2(rows, t * BK, nc, wave);
+    }
+    mx_issue(rows, t * BK, na, nb, wave, lane);
+    const uint8_t *ls;
+    int rs;   // LDS bytes between the scale entries of consecutive rows
+    if constexpr (SC16) {
+      ls = ((s / SCH) & 1 ? c1 : c0) + 2 * (s % SCH) + h;
+      rs = 16;
+    } else {
+      ls = lc + h;
+      rs = 4;
+    }
     i32x8 fa[2], fb[NB];
     int sa[2], sb[NB];
 #pragma unroll
@@ -222,7 +258,7 @@ __device__ __forceinline__ void mx_mainloop(const MxRows &rows, int Ktot, const 
       const u32x4 lo = *(const u32x4 *)(la + mx_off(row, h));
       const u32x4 hi = *(const u32x4 *)(la + mx_off(row, 2 + h));
       fa[i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-      sa[i] = ls[4 * row + h];
+      sa[i] = ls[rs * row];
     }
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
@@ -230,25 +266,31 @@ __device__ __forceinline__ void mx_mainloop(const MxRows &rows, int Ktot, const 
       const u32x4 lo = *(const u32x4 *)(lb + mx_off(row, h));
       const u32x4 hi = *(const u32x4 *)(lb + mx_off(row, 2 + h));
       fb[j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-      sb[j] = ls[4 * (BM + row) + h];
+      sb[j] = ls[rs * (BM + row)];
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < NB; ++j) acc[i][j] = mfma_mx_fp8(fa[i], fb[j], acc[i][j], sa[i], sb[j]);
   };
-  mx_issue(rows, 0, a0, b0, s0, wave, lane);
-  mx_issue(rows, (1 < S ? 1 : 0) * BK, a1, b1, s1, wave, lane);
+  if constexpr (SC16) {
+    mx_issue_sc16(rows, 0, c0, wave);
+  } else {
+    mx_issue_sc2(rows, 0, c0, wave);
+  }
+  mx_issue(rows, 0, a0, b0, wave, lane);
+  if constexpr (!SC16) mx_issue_sc2(rows, (1 < S ? 1 : 0) * BK, c1, wave);
+  mx_issue(rows, (1 < S ? 1 : 0) * BK, a1, b1, wave, lane);
   // whole ring turns, then the last one or two stages: the loop has a single
   // exit, which keeps each accumulator in one set of registers
   const int full = S - S % 3;
   for (int s = 0; s < full; s += 3) {
-    step(s, a0, b0, s0, a2, b2, s2);
-    step(s + 1, a1, b1, s1, a0, b0, s0);
-    step(s + 2, a2, b2, s2, a1, b1, s1);
+    step(s, a0, b0, c0, a2, b2, c2);
+    step(s + 1, a1, b1, c1, a0, b0, c0);
+    step(s + 2, a2, b2, c2, a1, b1, c1);
   }
-  if (S % 3 >= 1) step(full, a0, b0, s0, a2, b2, s2);
-  if (S % 3 == 2) step(full + 1, a1, b1, s1, a0, b0, s0);
+  if (S % 3 >= 1) step(full, a0, b0, c0, a2, b2, c2);
+  if (S % 3 == 2) step(full + 1, a1, b1, c1, a0, b0, c0);
   wait_vmcnt<0>();
   // the slots are reused by the next tile only after this barrier
   __builtin_amdgcn_s_barrier();
@@ -277,6 +319,7 @@ __device__ __forceinline__ float max32_lanes(float v) {
   return v;
 }
 
+template <bool SC16>
 __global__ __launch_bounds__(256) void k_gateup(MoeArgs p, const int32_t *meta,
                                                 const int32_t *sorted, const int32_t *tile_e,
                                                 const int32_t *tile_r, const int32_t *tile_n,
@@ -316,7 +359,7 @@ __global__ __launch_bounds__(256) void k_gateup(MoeArgs p, const int32_t *meta,
 #pragma unroll
   for (int i = 0; i < 2; ++i) acc[i][0] = acc[i][1] = f32x16{0};
   const int bsel[2] = {wn * 32, BNI + wn * 32};  // gate slab, up slab of the same columns
-  mx_mainloop<2>(rows, H, bsel, acc);
+  mx_mainloop<2, SC16>(rows, H, bsel, acc);
 
   // epilogue: h = silu(g) * u, MXFP8 block of 32 columns = this wave's 32 lanes
   const int col = i0 + wn * 32 + l32;
@@ -352,6 +395,7 @@ __global__ __launch_bounds__(256) void k_gateup(MoeArgs p, const int32_t *meta,
     }
 }
 
+template <bool SC16>
 __global__ __launch_bounds__(256) void k_down(MoeArgs p, const int32_t *meta, const int32_t *sorted,
                                               const int32_t *tile_e, const int32_t *tile_r,
                                               const int32_t *tile_n, const uint8_t *hq,
@@ -384,7 +428,7 @@ __global__ __launch_bounds__(256) void k_down(MoeArgs p, const int32_t *meta, co
 #pragma unroll
   for (int i = 0; i < 2; ++i) acc[i][0] = acc[i][1] = f32x16{0};
   const int bsel[2] = {wn * 64, wn * 64 + 32};
-  mx_mainloop<2>(rows, I, bsel, acc);
+  mx_mainloop<2, SC16>(rows, I, bsel, acc);
 
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -446,10 +490,20 @@ hipError_t launch_moe(const MoeArgs &p, hipStream_t stream) {
   hipLaunchKernelGGL(k_scan, dim3(1), dim3(256), 0, stream, counts, p.E, offs, meta, tile_e,
                      tile_r, tile_n);
   hipLaunchKernelGGL(k_scatter, dim3(rb), dim3(256), 0, stream, p.ids, L.R, offs, pos, sorted);
-  hipLaunchKernelGGL(k_gateup, dim3(p.I / BNI, L.maxtiles), dim3(256), 0, stream, p, meta, sorted,
-                     tile_e, tile_r, tile_n, hq, hs);
-  hipLaunchKernelGGL(k_down, dim3((p.H + BNH - 1) / BNH, L.maxtiles), dim3(256), 0, stream, p,
-                     meta, sorted, tile_e, tile_r, tile_n, hq, hs, y);
+  // scale rows of 16-byte multiples (K % 512 == 0) take the chunked scale loads
+  const dim3 gg(p.I / BNI, L.maxtiles), gd((p.H + BNH - 1) / BNH, L.maxtiles);
+  if (p.H % 512 == 0)
+    hipLaunchKernelGGL(k_gateup<true>, gg, dim3(256), 0, stream, p, meta, sorted, tile_e, tile_r,
+                       tile_n, hq, hs);
+  else
+    hipLaunchKernelGGL(k_gateup<false>, gg, dim3(256), 0, stream, p, meta, sorted, tile_e, tile_r,
+                       tile_n, hq, hs);
+  if (p.I % 512 == 0)
+    hipLaunchKernelGGL(k_down<true>, gd, dim3(256), 0, stream, p, meta, sorted, tile_e, tile_r,
+                       tile_n, hq, hs, y);
+  else
+    hipLaunchKernelGGL(k_down<false>, gd, dim3(256), 0, stream, p, meta, sorted, tile_e, tile_r,
+                       tile_n, hq, hs, y);
   hipLaunchKernelGGL(k_combine, dim3((unsigned)((TH4 + 255) / 256)), dim3(256), 0, stream, y, pos,
                      p.T, p.H, p.topk, p.out);
   return hipGetLastError();

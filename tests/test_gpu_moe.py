@@ -152,8 +152,11 @@ def _check_down_combine(inp, d, out, T, H, I, topk, tokens):
     check_bf16_vs(out[tokens], ref, bnd, what="moe out", extra=extra)
 
 
+# H or I a multiple of 512 takes the chunked scale loads (16 bytes of a scale
+# row per lane for 8 stages); the others the per-stage 2-byte loads
 @pytest.mark.parametrize("T,H,I,E,topk", [(64, 256, 128, 8, 4), (300, 128, 192, 6, 3),
-                                          (33, 64, 64, 16, 2)])
+                                          (33, 64, 64, 16, 2), (40, 1024, 512, 4, 2),
+                                          (24, 512, 1536, 3, 2)])
 def test_moe_stagewise(T, H, I, E, topk):
     inp = synth.moe(T, H, I, E, topk, seed=T + E)
     out, d = run_moe(inp, T, H, I, E, topk)
