@@ -193,37 +193,65 @@ __device__ __forceinline__ void mx_issue(const MxRows &r, int k0, uint8_t *la, u
 
 // Scale bytes.  When the scale rows are a multiple of 16 bytes long (K % 512
 // == 0), a lane loads its row's 16 bytes for 8 stages at once (chunk c:
-// stages 8c .. 8c+7), landing at ls + 16 * (64 wave + lane); otherwise it
-// loads the 2 bytes of one stage, landing in one dword per lane (low half) at
-// ls + 4 * (64 wave + lane).  Each such load touches one row per lane, and
-// the texture path's cost grows with the rows an instruction touches.
-__device__ __forceinline__ void mx_issue_sc16(const MxRows &r, int c, uint8_t *ls, int wave) {
-  __builtin_amdgcn_global_load_lds((gvoid *)(r.s + 16 * c), (lvoid *)(ls + 1024 * wave), 16, 0, 0);
+// stages 8c .. 8c+7) into registers and stores them a stage later to
+// ls + 16 * (64 wave + lane) (a plain store: a direct-to-LDS load into a
+// buffer chosen at run time would make every later LDS read wait for all
+// loads in flight); otherwise it loads the 2 bytes of one stage directly into
+// one dword per lane (low half) at ls + 4 * (64 wave + lane).  Each such
+// load touches one row per lane, and the texture path's cost grows with the
+// rows an instruction touches.
+__device__ __forceinline__ u32x4 mx_load_sc16(const MxRows &r, int c) {
+  return *(const u32x4 *)(r.s + 16 * c);
 }
 __device__ __forceinline__ void mx_issue_sc2(const MxRows &r, int k0, uint8_t *ls, int wave) {
   __builtin_amdgcn_global_load_lds((gvoid *)(r.s + k0 / 32), (lvoid *)(ls + 256 * wave), 2, 0, 0);
 }
 
-template <int NB, bool SC16>
-__device__ __forceinline__ void mx_mainloop(const MxRows &rows, int Ktot, const int bsel[NB],
-                                            f32x16 (&acc)[2][NB]) {
-  // three ring slots as separate arrays: the compiler can tell loads landing
-  // in one slot from reads of another.  Scales: two chunk buffers (SC16) or a
-  // slot per code slot.
-  constexpr int SC_BYTES = SC16 ? MX_SCC : MX_SCS;
+// A stage's MFMAs from one LDS slot: fragments of the wave's two A slabs and
+// NB B slabs, and their scales at ls + rs * row (A) / ls + rs * (BM + row) (B).
+template <int NB>
+__device__ __forceinline__ void mx_stage(const uint8_t *la, const uint8_t *lb, const uint8_t *ls, int rs,
+                                         const int bsel[NB], int wm, int h, int l32,
+                                         f32x16 (&acc)[2][NB]) {
+  i32x8 fa[2], fb[NB];
+  int sa[2], sb[NB];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = wm * 64 + i * 32 + l32;
+    const u32x4 lo = *(const u32x4 *)(la + mx_off(row, h));
+    const u32x4 hi = *(const u32x4 *)(la + mx_off(row, 2 + h));
+    fa[i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    sa[i] = ls[rs * row];
+  }
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const int row = bsel[j] + l32;
+    const u32x4 lo = *(const u32x4 *)(lb + mx_off(row, h));
+    const u32x4 hi = *(const u32x4 *)(lb + mx_off(row, 2 + h));
+    fb[j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    sb[j] = ls[rs * (BM + row)];
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[i][j] = mfma_mx_fp8(fa[i], fb[j], acc[i][j], sa[i], sb[j]);
+}
+
+// Per-stage scale loads (any K % 64 == 0): a three-slot ring of code and
+// scale slots, each a separate array so the compiler can tell loads landing
+// in one slot from reads of another; stage s+2 is loaded while stage s is
+// computed.
+template <int NB>
+__device__ __forceinline__ void mx_mainloop_sc2(const MxRows &rows, int Ktot, const int bsel[NB],
+                                                f32x16 (&acc)[2][NB]) {
   __shared__ __attribute__((aligned(1024))) uint8_t a0[MX_CODE], a1[MX_CODE], a2[MX_CODE];
   __shared__ __attribute__((aligned(1024))) uint8_t b0[MX_CODE], b1[MX_CODE], b2[MX_CODE];
-  __shared__ __attribute__((aligned(1024))) uint8_t c0[SC_BYTES], c1[SC_BYTES], c2[SC16 ? 16 : SC_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t c0[MX_SCS], c1[MX_SCS], c2[MX_SCS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, h = lane >> 5, l32 = lane & 31;
   const int S = Ktot / BK;
-  // direct loads per lane per stage: 4 code chunks (+ the scale pair when
-  // not SC16; a scale chunk is issued before the code loads of its first
-  // stage, so waiting for a stage's code loads covers it)
-  constexpr int LOADS = SC16 ? 4 : 5;
+  constexpr int LOADS = 5;   // direct loads per lane per stage: 4 code chunks, 1 scale pair
 
-  // one stage: stage s sits in (la, lb[, lc]); stage s+2 is issued into
-  // (na, nb[, nc]), the slot stage s-1 used
   auto step = [&](int s, const uint8_t *la, const uint8_t *lb, const uint8_t *lc, uint8_t *na,
                   uint8_t *nb, uint8_t *nc) {
     __builtin_amdgcn_sched_barrier(0);
@@ -232,54 +260,16 @@ __device__ __forceinline__ void mx_mainloop(const MxRows &rows, int Ktot, const 
     wait_vmcnt<LOADS>();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    // stages past the end reload the last one (never computed); a new scale
-    // chunk goes to the buffer whose stages every wave has finished
+    // stage s+2 into the slot stage s-1 used (every wave is past it); stages
+    // past the end reload the last one (never computed)
     const int t = s + 2 < S ? s + 2 : S - 1;
-    if constexpr (SC16) {
-      if ((s + 2) % SCH == 0 && s + 2 < S) mx_issue_sc16(rows, (s + 2) / SCH, ((s + 2) / SCH) & 1 ? c1 : c0, wave);
-    } else {
-      mx_issue_sc2(rows, t * BK, nc, wave);
-    }
+    mx_issue_sc2(rows, t * BK, nc, wave);
     mx_issue(rows, t * BK, na, nb, wave, lane);
-    const uint8_t *ls;
-    int rs;   // LDS bytes between the scale entries of consecutive rows
-    if constexpr (SC16) {
-      ls = ((s / SCH) & 1 ? c1 : c0) + 2 * (s % SCH) + h;
-      rs = 16;
-    } else {
-      ls = lc + h;
-      rs = 4;
-    }
-    i32x8 fa[2], fb[NB];
-    int sa[2], sb[NB];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int row = wm * 64 + i * 32 + l32;
-      const u32x4 lo = *(const u32x4 *)(la + mx_off(row, h));
-      const u32x4 hi = *(const u32x4 *)(la + mx_off(row, 2 + h));
-      fa[i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-      sa[i] = ls[rs * row];
-    }
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const int row = bsel[j] + l32;
-      const u32x4 lo = *(const u32x4 *)(lb + mx_off(row, h));
-      const u32x4 hi = *(const u32x4 *)(lb + mx_off(row, 2 + h));
-      fb[j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-      sb[j] = ls[rs * (BM + row)];
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < NB; ++j) acc[i][j] = mfma_mx_fp8(fa[i], fb[j], acc[i][j], sa[i], sb[j]);
+    mx_stage<NB>(la, lb, lc + h, 4, bsel, wm, h, l32, acc);
   };
-  if constexpr (SC16) {
-    mx_issue_sc16(rows, 0, c0, wave);
-  } else {
-    mx_issue_sc2(rows, 0, c0, wave);
-  }
+  mx_issue_sc2(rows, 0, c0, wave);
   mx_issue(rows, 0, a0, b0, wave, lane);
-  if constexpr (!SC16) mx_issue_sc2(rows, (1 < S ? 1 : 0) * BK, c1, wave);
+  mx_issue_sc2(rows, (1 < S ? 1 : 0) * BK, c1, wave);
   mx_issue(rows, (1 < S ? 1 : 0) * BK, a1, b1, wave, lane);
   // whole ring turns, then the last one or two stages: the loop has a single
   // exit, which keeps each accumulator in one set of registers
@@ -294,6 +284,70 @@ __device__ __forceinline__ void mx_mainloop(const MxRows &rows, int Ktot, const 
   wait_vmcnt<0>();
   // the slots are reused by the next tile only after this barrier
   __builtin_amdgcn_s_barrier();
+}
+
+// Scale chunks (K % 512 == 0): a four-slot code ring, stage s+3 loaded while
+// stage s is computed, and the loop walks one scale chunk (8 stages, two
+// ring turns) per iteration, so every slot is fixed at compile time.  Each
+// lane loads its row's 16 scale bytes of chunk c+1 into registers at the
+// start of chunk c and stores them (a plain LDS store) into the chunk buffer
+// not in use at its last stage; every read of a scale buffer then has a
+// known object that no direct-to-LDS load writes.
+template <int NB>
+__device__ __forceinline__ void mx_mainloop_sc16(const MxRows &rows, int Ktot, const int bsel[NB],
+                                                 f32x16 (&acc)[2][NB]) {
+  // (one array per slot, A codes then B codes: the compiler tracks only a
+  // few distinct targets of direct-to-LDS loads before it makes every LDS
+  // read wait for all of them)
+  __shared__ __attribute__((aligned(1024))) uint8_t q0[2 * MX_CODE], q1[2 * MX_CODE], q2[2 * MX_CODE],
+      q3[2 * MX_CODE];
+  __shared__ __attribute__((aligned(1024))) uint8_t cs[2][MX_SCC];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, h = lane >> 5, l32 = lane & 31;
+  const int S = Ktot / BK, nch = S / SCH;
+  // stage s has landed once at most the code loads of stages s+1 and s+2
+  // (4 each) are outstanding, plus, for the first three stages of a chunk,
+  // the next chunk's scale load (issued after their code loads)
+
+  uint8_t *const la[4] = {q0, q1, q2, q3};
+  uint8_t *const lb[4] = {q0 + MX_CODE, q1 + MX_CODE, q2 + MX_CODE, q3 + MX_CODE};
+  u32x4 scr = mx_load_sc16(rows, 0);
+  mx_issue(rows, 0, la[0], lb[0], wave, lane);
+  mx_issue(rows, (1 < S ? 1 : 0) * BK, la[1], lb[1], wave, lane);
+  mx_issue(rows, (2 < S ? 2 : S - 1) * BK, la[2], lb[2], wave, lane);
+  *(u32x4 *)(cs[0] + 16 * tid) = scr;   // ordered before the first reads by the first barrier
+  for (int c = 0; c < nch; ++c) {
+    scr = mx_load_sc16(rows, c + 1 < nch ? c + 1 : c);
+    const uint8_t *lsc = cs[c & 1] + h;
+#pragma unroll
+    for (int j = 0; j < SCH; ++j) {
+      const int s = SCH * c + j;
+      __builtin_amdgcn_sched_barrier(0);
+      if (j < 3)
+        wait_vmcnt<9>();
+      else
+        wait_vmcnt<8>();
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      // stage s+3 into the slot stage s-1 used (every wave is past it);
+      // stages past the end reload the last one (never computed)
+      mx_issue(rows, (s + 3 < S ? s + 3 : S - 1) * BK, la[(j + 3) & 3], lb[(j + 3) & 3], wave, lane);
+      if (j == SCH - 1) *(u32x4 *)(cs[(c + 1) & 1] + 16 * tid) = scr;
+      mx_stage<NB>(la[j & 3], lb[j & 3], lsc + 2 * j, 16, bsel, wm, h, l32, acc);
+    }
+  }
+  wait_vmcnt<0>();
+  // the slots are reused by the next tile only after this barrier
+  __builtin_amdgcn_s_barrier();
+}
+
+template <int NB, bool SC16>
+__device__ __forceinline__ void mx_mainloop(const MxRows &rows, int Ktot, const int bsel[NB],
+                                            f32x16 (&acc)[2][NB]) {
+  if constexpr (SC16)
+    mx_mainloop_sc16<NB>(rows, Ktot, bsel, acc);
+  else
+    mx_mainloop_sc2<NB>(rows, Ktot, bsel, acc);
 }
 
 // FP32 -> E4M3-FN byte, nearest even, saturating at +-448 (NaN -> 0x7F)
