@@ -179,14 +179,21 @@ def main():
         groups = M * N * (K // 16)
         traffic = traffic_for("gemm_w4a4.hip", "w4a4_m8192")
         out["w4a4"] = dict(ms=ms, tflops=tflops, gen_s=gen_s)
-        out["roofline"] = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK["fp8"],
-                           "unit": "TFLOP/s", "frac": round(tflops / PEAK["fp8"], 4),
-                           "traffic": traffic}
-        # the per-16 FP32 scale step: one fused multiply-add per output per group
+        # The exact FP8 route is bound by the vector ALU: one FP32 fused
+        # multiply-add per output per 16-element group (the group-scale step),
+        # M*N*K/16 per launch, against the MFMA work of 2 FP8 MFMAs per 32x32
+        # block and group.  `roofline` is that ALU work against the published
+        # FP32 vector peak (which counts packed FP32 instructions; this build
+        # emits none, so 78.6 TFLOP/s is the attainable half); `mfma_roofline`
+        # the GEMM flops against the FP8 MFMA peak (the metric's "% MFMA peak").
         alu = 2.0 * groups / (ms * 1e-3) / 1e12
-        out["alu_roofline"] = {"what": "per-group FP32 scale FMA (1 per output per 16 K)",
-                               "achieved": round(alu, 2), "peak": PEAK_VALU_F32, "unit": "TFLOP/s",
-                               "frac": round(alu / PEAK_VALU_F32, 4)}
+        out["roofline"] = {"bound": "alu", "achieved": round(alu, 2), "peak": PEAK["fp32"],
+                           "unit": "TFLOP/s", "frac": round(alu / PEAK["fp32"], 4),
+                           "traffic": traffic,
+                           "what": "per-group FP32 scale FMAs, M*N*K/16 per launch, 2 flops each",
+                           "frac_of_unpacked_fp32": round(alu / PEAK_VALU_F32, 4)}
+        out["mfma_roofline"] = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK["fp8"],
+                                "unit": "TFLOP/s", "frac": round(tflops / PEAK["fp8"], 4)}
         # sampled parity of the timed output against the oracle (bench sanity)
         rng = np.random.default_rng(1)
         pm, pn = rng.integers(0, M, 64), rng.integers(0, N, 64)
@@ -309,7 +316,7 @@ def main():
                    "M": M, "N": N, "K": K, "parallelism": "single GPU"},
         "roofline": out.get("roofline"),
         "cpu_baseline": cpu,
-        "alu_roofline": out.get("alu_roofline"),
+        "mfma_roofline": out.get("mfma_roofline"),
         "parity_sample": par,
         "decode": out.get("decode"),
         "bf16": out.get("bf16"),
