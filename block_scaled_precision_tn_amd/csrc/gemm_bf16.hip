@@ -54,6 +54,17 @@ __device__ __forceinline__ float e2m1_to_f32(uint32_t c) {
   return __builtin_bit_cast(float, bits);
 }
 
+// One direct-to-LDS load of 16 bytes per lane: lane i's bytes land at
+// lds + 16 i.  Written as inline assembly so the compiler does not track it:
+// for the builtin form it cannot always tell which LDS slot a load fills and
+// then makes every LDS read wait for all loads in flight.  The kernels wait
+// for these loads with explicit vmcnt counts (they complete in issue order).
+__device__ __forceinline__ void dma16(const void *g, uint8_t *lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lvoid *)lds);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0)
+               : "memory", "m0");
+}
+
 // Issue the direct-to-LDS loads of one BF16 operand tile (R rows x 64 K) at
 // k0 into `lds`.  Each wave instruction fills 1 KB = 8 rows; lane i fills LDS
 // position (row 8b + i / 8, slot i % 8), which holds global chunk
@@ -73,8 +84,7 @@ __device__ __forceinline__ void dma_tile(const uint16_t *src, int rows, int K, i
     grow = grow < rows ? grow : rows - 1;
     int k = k0 + 8 * chunk;
     k = k < K ? k : K - 8;
-    __builtin_amdgcn_global_load_lds((gvoid *)(src + (int64_t)grow * K + k),
-                                     (lvoid *)(lds + 1024 * b), 16, 0, 0);
+    dma16(src + (int64_t)grow * K + k, lds + 1024 * b);
   }
 }
 
@@ -174,7 +184,10 @@ __global__ __launch_bounds__(NTHR, 1) void bf16_gemm_kernel(Bf16Args p) {
     // the bare s_barrier: a fenced one would wait for every load in flight.
     wait_vmcnt<WQ ? LOADS + 2 : LOADS>();
     if (s == S - 1 && p.K % BK != 0) {
+      // every thread's loads of the stage have landed before any thread
+      // zeroes chunks that another thread loaded
       wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
       fix_k_tail<BM>(la, p.K, s * BK, tid);
       if (!WQ) fix_k_tail<BN>(lw, p.K, s * BK, tid);
     }
