@@ -216,19 +216,89 @@ __global__ __launch_bounds__(NTHR, 1) void bf16_gemm_kernel(Bf16Args p) {
         for (int j = 0; j < 2; ++j) acc[i][j] = mfma_bf16(fa[kk & 1][i], fw[kk & 1][j], acc[i][j]);
     }
   };
-  if (WQ) wq_load(p, n0, 0, tid, wr);
-  issue(0, la0, lw0);
-  issue(1, la1, lw1);
-  // whole ring turns, then the last one or two stages: the loop has a single
-  // exit, which keeps each accumulator in one set of registers
-  const int full = S - S % 3;
-  for (int s = 0; s < full; s += 3) {
-    step(s, la0, lw0, la2, lw2);
-    step(s + 1, la1, lw1, la0, lw0);
-    step(s + 2, la2, lw2, la1, lw1);
+  if constexpr (WQ) {
+    wq_load(p, n0, 0, tid, wr);
+    issue(0, la0, lw0);
+    issue(1, la1, lw1);
+    // whole ring turns, then the last one or two stages: the loop has a single
+    // exit, which keeps each accumulator in one set of registers
+    const int full = S - S % 3;
+    for (int s = 0; s < full; s += 3) {
+      step(s, la0, lw0, la2, lw2);
+      step(s + 1, la1, lw1, la0, lw0);
+      step(s + 2, la2, lw2, la1, lw1);
+    }
+    if (S % 3 >= 1) step(full, la0, lw0, la2, lw2);
+    if (S % 3 == 2) step(full + 1, la1, lw1, la0, lw0);
+  } else {
+    // BF16 x BF16, pipelined across stages: the MFMAs of a stage's last
+    // K-step are issued after the wave has met the others at the barrier for
+    // the next stage and read that stage's first fragments, so the barrier
+    // and those reads overlap the MFMAs in flight.  Past that barrier no wave
+    // reads the current slot any more, so it is refilled right away with the
+    // stage three ahead: three stages are in flight in three slots.
+    u32x4 fa[2][2], fw[2][2];
+    auto frag = [&](const uint8_t *la, const uint8_t *lw, int kk, int b) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        fa[b][i] = *(const u32x4 *)(la + swz(wm * 64 + i * 32 + l32, 2 * kk + h));
+        fw[b][i] = *(const u32x4 *)(lw + swz(wn * 64 + i * 32 + l32, 2 * kk + h));
+      }
+    };
+    auto mfmas = [&](int b) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma_bf16(fa[b][i], fw[b][j], acc[i][j]);
+    };
+    // make stage t's slot readable: its loads landed (one or two later
+    // stages' loads may still be in flight), the K tail zeroed, every wave
+    // past the barrier
+    auto ready = [&](int t, uint8_t *la, uint8_t *lw, bool two_after) {
+      if (two_after)
+        wait_vmcnt<2 * LOADS>();
+      else
+        wait_vmcnt<LOADS>();
+      if (t == S - 1 && p.K % BK != 0) {
+        wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        fix_k_tail<BM>(la, p.K, t * BK, tid);
+        fix_k_tail<BN>(lw, p.K, t * BK, tid);
+      }
+      wait_lgkm0();
+      __builtin_amdgcn_s_barrier();
+    };
+    // stage s computed from (la, lw); stage s+1 waits in (na, nw)
+    auto step2 = [&](int s, uint8_t *la, uint8_t *lw, uint8_t *na, uint8_t *nw) {
+#pragma unroll
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (kk + 1 < BK / 16) {
+          frag(la, lw, kk + 1, (kk + 1) & 1);
+        } else if (s + 1 < S) {
+          ready(s + 1, na, nw, false);
+          __builtin_amdgcn_sched_barrier(0);
+          issue(s + 3, la, lw);
+          frag(na, nw, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(kk & 1);
+      }
+    };
+    issue(0, la0, lw0);
+    issue(1, la1, lw1);
+    issue(2, la2, lw2);
+    ready(0, la0, lw0, true);
+    frag(la0, lw0, 0, 0);
+    const int full = S - S % 3;
+    for (int s = 0; s < full; s += 3) {
+      step2(s, la0, lw0, la1, lw1);
+      step2(s + 1, la1, lw1, la2, lw2);
+      step2(s + 2, la2, lw2, la0, lw0);
+    }
+    if (S % 3 >= 1) step2(full, la0, lw0, la1, lw1);
+    if (S % 3 == 2) step2(full + 1, la1, lw1, la2, lw2);
   }
-  if (S % 3 >= 1) step(full, la0, lw0, la2, lw2);
-  if (S % 3 == 2) step(full + 1, la1, lw1, la0, lw0);
   wait_vmcnt<0>();
 
   const float gs = WQ ? *p.Sw : 1.0f;
