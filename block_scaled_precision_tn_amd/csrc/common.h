@@ -145,6 +145,27 @@ __device__ __forceinline__ void wait_lgkm0() {
   __builtin_amdgcn_s_waitcnt(63 | (3 << 14) | (7 << 4) | (0 << 8));
 }
 
+// Direct-to-LDS loads (global_load_lds): lane i's bytes land at
+// lds + size * i (sizes below 4 fill one dword per lane, zero-extended).
+// Written as inline assembly so the compiler does not track them: for the
+// builtin form it cannot always tell which LDS buffer a load fills and then
+// makes every LDS read wait for all loads in flight.  Kernels wait for these
+// loads with explicit vmcnt counts (loads complete in issue order).
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ uint32_t lds_addr(const void *lds) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void *)lds);
+}
+__device__ __forceinline__ void dma16(const void *g, const void *lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g),
+               "s"(lds_addr(lds))
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma2(const void *g, const void *lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_ushort %0, off" ::"v"(g),
+               "s"(lds_addr(lds))
+               : "memory", "m0");
+}
+
 // row held by accumulator register r of lane l (see the layout note above)
 __device__ __forceinline__ int acc_row(int r, int lane) {
   return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);

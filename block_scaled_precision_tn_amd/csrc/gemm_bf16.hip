@@ -33,8 +33,6 @@ constexpr int NSTAGE = 3;            // LDS ring depth
 constexpr int ROWB = BK * 2;         // bytes per LDS row (64 BF16)
 constexpr int STAGE_A = BM * ROWB, STAGE_W = BN * ROWB;
 
-typedef __attribute__((address_space(1))) void gvoid;
-typedef __attribute__((address_space(3))) void lvoid;
 
 // 16-byte chunk `chunk` of tile row `row`: rows are 128 bytes, and the chunk
 // is XOR-ed with (row / 2) % 8, so any 16 consecutive rows read at one chunk
@@ -52,17 +50,6 @@ __device__ __forceinline__ float e2m1_to_f32(uint32_t c) {
                             : (mag == 1u ? 0x3F000000u : 0u);
   bits |= (c & 8u) << 28;
   return __builtin_bit_cast(float, bits);
-}
-
-// One direct-to-LDS load of 16 bytes per lane: lane i's bytes land at
-// lds + 16 i.  Written as inline assembly so the compiler does not track it:
-// for the builtin form it cannot always tell which LDS slot a load fills and
-// then makes every LDS read wait for all loads in flight.  The kernels wait
-// for these loads with explicit vmcnt counts (they complete in issue order).
-__device__ __forceinline__ void dma16(const void *g, uint8_t *lds) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lvoid *)lds);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0)
-               : "memory", "m0");
 }
 
 // Issue the direct-to-LDS loads of one BF16 operand tile (R rows x 64 K) at

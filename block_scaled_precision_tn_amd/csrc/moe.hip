@@ -160,8 +160,6 @@ __global__ void k_scatter(const int32_t *ids, int R, const int32_t *offs, int32_
 // bytes (A rows, then B rows) arrive 8 stages at a time when K % 512 == 0,
 // else per stage (see mx_issue_sc16 / mx_issue_sc2).  A rows are gathered:
 // every lane holds the global row pointers of the rows it loads.
-typedef __attribute__((address_space(1))) void gvoid;
-typedef __attribute__((address_space(3))) void lvoid;
 
 constexpr int MX_CODE = BM * BK;          // bytes of one operand's codes per stage
 constexpr int SCH = 8;                    // stages per scale chunk (K % 512 == 0)
@@ -186,8 +184,8 @@ __device__ __forceinline__ void mx_issue(const MxRows &r, int k0, uint8_t *la, u
   for (int j = 0; j < 2; ++j) {
     const int blk = 2 * wave + j, row = 16 * blk + (lane >> 2), slot = lane & 3;
     const int chunk = slot ^ ((row >> 2) & 3);
-    __builtin_amdgcn_global_load_lds((gvoid *)(r.a[j] + k0 + 16 * chunk), (lvoid *)(la + 1024 * blk), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((gvoid *)(r.b[j] + k0 + 16 * chunk), (lvoid *)(lb + 1024 * blk), 16, 0, 0);
+    dma16(r.a[j] + k0 + 16 * chunk, la + 1024 * blk);
+    dma16(r.b[j] + k0 + 16 * chunk, lb + 1024 * blk);
   }
 }
 
@@ -204,7 +202,7 @@ __device__ __forceinline__ u32x4 mx_load_sc16(const MxRows &r, int c) {
   return *(const u32x4 *)(r.s + 16 * c);
 }
 __device__ __forceinline__ void mx_issue_sc2(const MxRows &r, int k0, uint8_t *ls, int wave) {
-  __builtin_amdgcn_global_load_lds((gvoid *)(r.s + k0 / 32), (lvoid *)(ls + 256 * wave), 2, 0, 0);
+  dma2(r.s + k0 / 32, ls + 256 * wave);
 }
 
 // A stage's MFMAs from one LDS slot: fragments of the wave's two A slabs and
