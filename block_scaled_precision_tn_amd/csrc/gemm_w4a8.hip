@@ -232,12 +232,36 @@ __device__ __forceinline__ void wait_ranges_left(int left) {
   }
 }
 
+// Workgroup id -> (weight tile, split).  A 128-byte line of a row's scale
+// bytes covers SPL consecutive splits (SPL * RPW ranges of 16 scale bytes);
+// the SPL workgroups that share those lines are given ids that are equal
+// modulo 8, the number of XCDs that take workgroups round-robin, so they run
+// on one XCD and the lines come from HBM once into its L2 rather than once
+// per workgroup.  Ids that map past the last split return at once.
+constexpr int XCDS = 8;
+constexpr int SPL = 128 / (RPW * SB);
+__device__ __forceinline__ bool split_of(int id, int tiles, int ks, int &nt, int &kc) {
+  const int kq = (ks + SPL - 1) / SPL;                     // line groups per tile
+  const int x = id % XCDS, slot = id / XCDS;
+  const int lg = x + XCDS * (slot / SPL);
+  if (lg >= tiles * kq) return false;
+  nt = lg / kq;
+  kc = (lg % kq) * SPL + slot % SPL;
+  return kc < ks;
+}
+
+int split_grid(int tiles, int ks) {
+  const int lgs = tiles * ((ks + SPL - 1) / SPL);
+  return XCDS * SPL * ((lgs + XCDS - 1) / XCDS);
+}
+
 template <int QUADS, bool SFAST>
 __global__ __launch_bounds__(256) void w4a8_decode_kernel(W4A8Args p, int ks, float *part) {
   constexpr int MT = Acc<QUADS>::MT;
   __shared__ __attribute__((aligned(16))) Tile<MT> tile;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
-  const int nt = blockIdx.x, kc = blockIdx.y;
+  int nt, kc;
+  if (!split_of(blockIdx.x, (p.N + NT - 1) / NT, ks, nt, kc)) return;
   const int n0 = nt * NT;
   const int nrange = (p.K + KR - 1) / KR;
   const int rbeg = kc * RPW;
@@ -336,7 +360,7 @@ int splits(int64_t K) { return (int)(((K + KR - 1) / KR + RPW - 1) / RPW); }
 
 template <int QUADS>
 void launch_one(const W4A8Args &p, int ks, float *part, hipStream_t stream) {
-  dim3 grid((p.N + NT - 1) / NT, ks);
+  const dim3 grid(split_grid((p.N + NT - 1) / NT, ks));
   if (p.K % 256 == 0)
     hipLaunchKernelGGL((w4a8_decode_kernel<QUADS, true>), grid, dim3(256), 0, stream, p, ks, part);
   else
