@@ -31,7 +31,9 @@
 //     launch.)
 // Tokens sit on the MFMA's A side, padded to 32: lanes of token rows >= M
 // read row 0 (those MFMA rows are never stored), and only the accumulator
-// registers that hold real tokens are scaled.  M > 32 runs in slices of 32.
+// registers that hold real tokens are scaled.  Up to 128 tokens go through
+// one launch as up to four 32-token blocks, each weight fragment converted
+// once for all of them; larger M runs in slices of 128.
 #include "common.h"
 #include "kernels.h"
 
@@ -41,7 +43,7 @@ namespace {
 constexpr int NT = 128;       // weight rows per workgroup (4 waves x 32)
 constexpr int KR = 256;       // K-elements per range
 constexpr int RPW = 2;        // ranges per workgroup, all requested at once
-constexpr int MS = 32;        // tokens per launch
+constexpr int MS = 128;       // tokens per launch (up to 4 blocks of 32)
 
 constexpr int ROWB = KR / 2;          // code bytes per weight row per range
 constexpr int CHUNKS = ROWB / 16;     // 16-byte chunks per code row (2 groups each)
@@ -175,33 +177,41 @@ __device__ __forceinline__ void range_store(Tile<MT> &tile, int M, int klen, int
 
 // np pairs of 16-element groups (2 groups per code chunk) from the LDS tile
 // QUADS = accumulator quads in use (8 tokens each); 0 means one token: only
-// register 0 (token 0 in the lanes of K-half 0) is updated and stored.
+// register 0 (token 0 in the lanes of K-half 0) is updated and stored.  Up to
+// 4 quads fill one 32-token block; QUADS = 8 and 16 are 2 and 4 full blocks
+// (64 and 128 tokens), each code fragment converted once for all blocks.
 template <int QUADS>
 struct Acc {
   static constexpr int MT = QUADS == 0 ? 8 : 8 * QUADS;   // token rows in the LDS tile
-  static constexpr int NREG = QUADS == 0 ? 1 : 4 * QUADS; // accumulator registers in use
+  static constexpr int TB = QUADS <= 4 ? 1 : QUADS / 4;   // 32-token blocks
+  static constexpr int NREG = QUADS == 0 ? 1 : (QUADS <= 4 ? 4 * QUADS : 16);  // registers in use per block
 };
 
 template <int QUADS, bool FULL>
 __device__ __forceinline__ void compute_range(const Tile<Acc<QUADS>::MT> &tile, int row, int trow, int h, int np,
-                                              f32x16 &acc) {
+                                              f32x16 (&acc)[Acc<QUADS>::TB]) {
+  constexpr int TB = Acc<QUADS>::TB;
   const uint8_t *wtile = tile.w + 8 * h;
   const uint8_t *arow = tile.a + trow * AROW + 16 * h;
   const float *srow = tile.s + row * SROWF;
   const f32x16 zero = {0};
   auto pair = [&](int c) {
     const uint64_t cw = *(const uint64_t *)(wtile + woff(row, c));
-    const u32x4 av = *(const u32x4 *)(arow + 32 * c);
     const f32x2 sc = *(const f32x2 *)(srow + 2 * c);
     const float s0 = sc[0], s1 = sc[1];
-    const uint64_t a0 = (uint64_t)av[0] | ((uint64_t)av[1] << 32);
-    const uint64_t a1 = (uint64_t)av[2] | ((uint64_t)av[3] << 32);
-    const f32x16 p0 = mfma_fp8(a0, nvfp4x8_to_e4m3x8((uint32_t)cw), zero);
-    const f32x16 p1 = mfma_fp8(a1, nvfp4x8_to_e4m3x8((uint32_t)(cw >> 32)), zero);
+    const uint64_t w0 = nvfp4x8_to_e4m3x8((uint32_t)cw), w1 = nvfp4x8_to_e4m3x8((uint32_t)(cw >> 32));
 #pragma unroll
-    for (int r = 0; r < Acc<QUADS>::NREG; ++r) acc[r] = __builtin_fmaf(s0, p0[r], acc[r]);
+    for (int b = 0; b < TB; ++b) {
+      const u32x4 av = *(const u32x4 *)(arow + 32 * AROW * b + 32 * c);
+      const uint64_t a0 = (uint64_t)av[0] | ((uint64_t)av[1] << 32);
+      const uint64_t a1 = (uint64_t)av[2] | ((uint64_t)av[3] << 32);
+      const f32x16 p0 = mfma_fp8(a0, w0, zero);
+      const f32x16 p1 = mfma_fp8(a1, w1, zero);
 #pragma unroll
-    for (int r = 0; r < Acc<QUADS>::NREG; ++r) acc[r] = __builtin_fmaf(s1, p1[r], acc[r]);
+      for (int r = 0; r < Acc<QUADS>::NREG; ++r) acc[b][r] = __builtin_fmaf(s0, p0[r], acc[b][r]);
+#pragma unroll
+      for (int r = 0; r < Acc<QUADS>::NREG; ++r) acc[b][r] = __builtin_fmaf(s1, p1[r], acc[b][r]);
+    }
   };
   if constexpr (FULL) {
 #pragma unroll
@@ -213,7 +223,7 @@ __device__ __forceinline__ void compute_range(const Tile<Acc<QUADS>::MT> &tile, 
 
 template <int QUADS>
 __device__ __forceinline__ void compute_any(const Tile<Acc<QUADS>::MT> &tile, int row, int trow, int h, int klen,
-                                            f32x16 &acc) {
+                                            f32x16 (&acc)[Acc<QUADS>::TB]) {
   if (klen == KR)
     compute_range<QUADS, true>(tile, row, trow, h, CHUNKS, acc);
   else
@@ -255,6 +265,8 @@ int split_grid(int tiles, int ks) {
   return XCDS * SPL * ((lgs + XCDS - 1) / XCDS);
 }
 
+int splits(int64_t K) { return (int)(((K + KR - 1) / KR + RPW - 1) / RPW); }
+
 template <int QUADS, bool SFAST>
 __global__ __launch_bounds__(256) void w4a8_decode_kernel(W4A8Args p, int ks, float *part) {
   constexpr int MT = Acc<QUADS>::MT;
@@ -267,9 +279,14 @@ __global__ __launch_bounds__(256) void w4a8_decode_kernel(W4A8Args p, int ks, fl
   const int rbeg = kc * RPW;
   const int rend = rbeg + RPW < nrange ? rbeg + RPW : nrange;
 
+  constexpr int TB = Acc<QUADS>::TB;
   const int row = wave * 32 + l32;
-  const int trow = l32 < p.M ? l32 : 0;
-  f32x16 acc = {0};
+  // (with one block, token rows past M read row 0: never stored; with several
+  // blocks every tile row exists and rows past M hold zeros)
+  const int trow = TB > 1 || l32 < p.M ? l32 : 0;
+  f32x16 acc[TB];
+#pragma unroll
+  for (int b = 0; b < TB; ++b) acc[b] = f32x16{0};
 
   // All of the workgroup's ranges (at most RPW) are requested at once into
   // register buffers, so the whole weight stream is in flight from the start;
@@ -310,24 +327,28 @@ __global__ __launch_bounds__(256) void w4a8_decode_kernel(W4A8Args p, int ks, fl
     if (n >= p.N) return;
     const float sw = *p.Sw;
 #pragma unroll
-    for (int r = 0; r < Acc<QUADS>::NREG; ++r) {
-      const int t = acc_row(r, lane);
-      if (t >= p.M) continue;
-      const float v = acc[r] * (p.atok[t] * sw);
-      if (p.out_f32)
-        ((float *)p.C)[(int64_t)t * p.N + n] = v;
-      else
-        ((uint16_t *)p.C)[(int64_t)t * p.N + n] = (uint16_t)f32_to_bf16_rne(v);
-    }
+    for (int b = 0; b < TB; ++b)
+#pragma unroll
+      for (int r = 0; r < Acc<QUADS>::NREG; ++r) {
+        const int t = 32 * b + acc_row(r, lane);
+        if (t >= p.M) continue;
+        const float v = acc[b][r] * (p.atok[t] * sw);
+        if (p.out_f32)
+          ((float *)p.C)[(int64_t)t * p.N + n] = v;
+        else
+          ((uint16_t *)p.C)[(int64_t)t * p.N + n] = (uint16_t)f32_to_bf16_rne(v);
+      }
     return;
   }
 
   if (n < p.N) {
 #pragma unroll
-    for (int r = 0; r < Acc<QUADS>::NREG; ++r) {
-      const int t = acc_row(r, lane);
-      if (t < p.M) part[((int64_t)kc * p.M + t) * p.N + n] = acc[r];
-    }
+    for (int b = 0; b < TB; ++b)
+#pragma unroll
+      for (int r = 0; r < Acc<QUADS>::NREG; ++r) {
+        const int t = 32 * b + acc_row(r, lane);
+        if (t < p.M) part[((int64_t)kc * p.M + t) * p.N + n] = acc[b][r];
+      }
   }
 }
 
@@ -355,8 +376,6 @@ __global__ __launch_bounds__(64) void w4a8_splitk_reduce(W4A8Args p, int ks, con
   else
     ((uint16_t *)p.C)[i] = (uint16_t)f32_to_bf16_rne(v);
 }
-
-int splits(int64_t K) { return (int)(((K + KR - 1) / KR + RPW - 1) / RPW); }
 
 template <int QUADS>
 void launch_one(const W4A8Args &p, int ks, float *part, hipStream_t stream) {
@@ -387,7 +406,9 @@ hipError_t launch_w4a8(const W4A8Args &p0, hipStream_t stream) {
     p.aq = p0.aq + (int64_t)m0 * p0.K;
     p.atok = p0.atok + m0;
     p.C = (char *)p0.C + (int64_t)m0 * p0.N * (p0.out_f32 ? 4 : 2);
-    if (p.M > 24) launch_one<4>(p, ks, part, stream);
+    if (p.M > 64) launch_one<16>(p, ks, part, stream);
+    else if (p.M > 32) launch_one<8>(p, ks, part, stream);
+    else if (p.M > 24) launch_one<4>(p, ks, part, stream);
     else if (p.M > 16) launch_one<3>(p, ks, part, stream);
     else if (p.M > 8) launch_one<2>(p, ks, part, stream);
     else if (p.M > 1) launch_one<1>(p, ks, part, stream);
