@@ -35,7 +35,7 @@ constexpr int BNH = 128;      // hidden columns per down tile
 constexpr int BK = 64;        // K per LDS stage (two 32-element scale blocks)
 
 struct Layout {
-  size_t counts, offs, meta, sorted, pos, tile_e, tile_r, tile_n, hq, hs, y, total;
+  size_t counts, offs, meta, sorted, pos, wsorted, tile_e, tile_r, tile_n, hq, hs, y, total;
   int R, maxtiles;
 };
 
@@ -51,6 +51,7 @@ Layout layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk) {
   L.meta = o;   o += up256(sizeof(int32_t) * 4);                 // [0] = number of tiles
   L.sorted = o; o += up256(sizeof(int32_t) * (size_t)L.R);
   L.pos = o;    o += up256(sizeof(int32_t) * (size_t)L.R);          // sorted row of each entry
+  L.wsorted = o; o += up256(sizeof(float) * (size_t)L.R);           // routing weight of each sorted row
   L.tile_e = o; o += up256(sizeof(int32_t) * (size_t)L.maxtiles);
   L.tile_r = o; o += up256(sizeof(int32_t) * (size_t)L.maxtiles);
   L.tile_n = o; o += up256(sizeof(int32_t) * (size_t)L.maxtiles);
@@ -133,9 +134,9 @@ __global__ __launch_bounds__(256) void k_scan(const uint32_t *counts, int E, int
   }
 }
 
-// sorted row of each entry, and the entry of each sorted row
-__global__ void k_scatter(const int32_t *ids, int R, const int32_t *offs, int32_t *pos,
-                          int32_t *sorted) {
+// sorted row of each entry, and the entry and routing weight of each sorted row
+__global__ void k_scatter(const int32_t *ids, const float *tw, int R, const int32_t *offs,
+                          int32_t *pos, int32_t *sorted, float *wsorted) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < R) {
     const int rk = pos[i];                     // rank from k_count, or -1
@@ -143,6 +144,7 @@ __global__ void k_scatter(const int32_t *ids, int R, const int32_t *offs, int32_
       const int p = offs[ids[i]] + rk;
       pos[i] = p;
       sorted[p] = i;
+      wsorted[p] = tw[i];
     }
   }
 }
@@ -448,10 +450,11 @@ __global__ __launch_bounds__(256) void k_gateup(MoeArgs p, const int32_t *meta,
 }
 
 template <bool SC16>
-__global__ __launch_bounds__(256) void k_down(MoeArgs p, const int32_t *meta, const int32_t *sorted,
+__global__ __launch_bounds__(256) void k_down(MoeArgs p, const int32_t *meta, const float *wsorted,
                                               const int32_t *tile_e, const int32_t *tile_r,
                                               const int32_t *tile_n, const uint8_t *hq,
                                               const uint8_t *hs, float *y) {
+  __shared__ float s_w[256];   // routing weight of tile row t at s_w[t] (and s_w[128 + t])
   const int tile = blockIdx.y;
   if (tile >= meta[0]) return;
   const int e = tile_e[tile], r0 = tile_r[tile], nrows = tile_n[tile];
@@ -459,6 +462,9 @@ __global__ __launch_bounds__(256) void k_down(MoeArgs p, const int32_t *meta, co
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31;
   const int H = p.H, I = p.I;
+  // the tile rows' routing weights, requested before the main loop's loads
+  // (so they have landed long before the epilogue needs them)
+  const float wrow = wsorted[r0 + ((tid & 127) < nrows ? (tid & 127) : 0)];
 
   // A rows: sorted h rows (rows past the tile read its first row: never
   // stored); B rows: w2[e] rows n0 + row (past H: the last row, never stored)
@@ -481,6 +487,8 @@ __global__ __launch_bounds__(256) void k_down(MoeArgs p, const int32_t *meta, co
   for (int i = 0; i < 2; ++i) acc[i][0] = acc[i][1] = f32x16{0};
   const int bsel[2] = {wn * 64, wn * 64 + 32};
   mx_mainloop<2, SC16>(rows, I, bsel, acc);
+  s_w[tid] = wrow;
+  __syncthreads();
 
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -488,7 +496,7 @@ __global__ __launch_bounds__(256) void k_down(MoeArgs p, const int32_t *meta, co
     for (int r = 0; r < 16; ++r) {
       const int row = wm * 64 + i * 32 + acc_row(r, lane);
       if (row >= nrows) continue;
-      const float w = p.tw[sorted[r0 + row]];
+      const float w = s_w[row];
       float *yrow = y + (int64_t)(r0 + row) * H;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
@@ -541,7 +549,9 @@ hipError_t launch_moe(const MoeArgs &p, hipStream_t stream) {
                      counts, pos);
   hipLaunchKernelGGL(k_scan, dim3(1), dim3(256), 0, stream, counts, p.E, offs, meta, tile_e,
                      tile_r, tile_n);
-  hipLaunchKernelGGL(k_scatter, dim3(rb), dim3(256), 0, stream, p.ids, L.R, offs, pos, sorted);
+  float *wsorted = (float *)(w + L.wsorted);
+  hipLaunchKernelGGL(k_scatter, dim3(rb), dim3(256), 0, stream, p.ids, p.tw, L.R, offs, pos, sorted,
+                     wsorted);
   // scale rows of 16-byte multiples (K % 512 == 0) take the chunked scale loads
   const dim3 gg(p.I / BNI, L.maxtiles), gd((p.H + BNH - 1) / BNH, L.maxtiles);
   if (p.H % 512 == 0)
@@ -551,10 +561,10 @@ hipError_t launch_moe(const MoeArgs &p, hipStream_t stream) {
     hipLaunchKernelGGL(k_gateup<false>, gg, dim3(256), 0, stream, p, meta, sorted, tile_e, tile_r,
                        tile_n, hq, hs);
   if (p.I % 512 == 0)
-    hipLaunchKernelGGL(k_down<true>, gd, dim3(256), 0, stream, p, meta, sorted, tile_e, tile_r,
+    hipLaunchKernelGGL(k_down<true>, gd, dim3(256), 0, stream, p, meta, wsorted, tile_e, tile_r,
                        tile_n, hq, hs, y);
   else
-    hipLaunchKernelGGL(k_down<false>, gd, dim3(256), 0, stream, p, meta, sorted, tile_e, tile_r,
+    hipLaunchKernelGGL(k_down<false>, gd, dim3(256), 0, stream, p, meta, wsorted, tile_e, tile_r,
                        tile_n, hq, hs, y);
   hipLaunchKernelGGL(k_combine, dim3((unsigned)((TH4 + 255) / 256)), dim3(256), 0, stream, y, pos,
                      p.T, p.H, p.topk, p.out);
