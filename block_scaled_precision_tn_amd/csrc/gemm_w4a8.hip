@@ -353,24 +353,24 @@ __global__ __launch_bounds__(256) void w4a8_decode_kernel(W4A8Args p, int ks, fl
 }
 
 // C[t,n] = (sum over splits s = 0..ks-1, in order, of part[s,t,n]) * a_tok[t] * S_w.
-// Partials are requested CH at a time (all of them when ks <= CH, so a
-// decode-sized reduction waits on one memory latency).
+// One element per thread.  The scales and the first CH partials are all
+// requested up front (addresses past ks repeat the last split and are not
+// added), so a decode-sized reduction waits on one memory latency.
 __global__ __launch_bounds__(64) void w4a8_splitk_reduce(W4A8Args p, int ks, const float *part) {
-  constexpr int CH = 16;
+  constexpr int CH = 32;
   const int64_t i = (int64_t)blockIdx.x * 64 + threadIdx.x;
   const int64_t mn = (int64_t)p.M * p.N;
   if (i >= mn) return;
-  const int t = (int)(i / p.N);
+  const int t = mn <= 0x7FFFFFFF ? (int)((uint32_t)i / (uint32_t)p.N) : (int)(i / p.N);
+  const float scale = p.atok[t] * *p.Sw;
+  float x[CH];
+#pragma unroll
+  for (int j = 0; j < CH; ++j) x[j] = part[(int64_t)(j < ks ? j : ks - 1) * mn + i];
   float v = 0.0f;
-  for (int s0 = 0; s0 < ks; s0 += CH) {
-    float x[CH];
 #pragma unroll
-    for (int j = 0; j < CH; ++j) x[j] = part[(int64_t)(s0 + j < ks ? s0 + j : s0) * mn + i];
-#pragma unroll
-    for (int j = 0; j < CH; ++j)
-      if (s0 + j < ks) v += x[j];
-  }
-  v *= p.atok[t] * *p.Sw;
+  for (int j = 0; j < CH; ++j) v = j < ks ? v + x[j] : v;
+  for (int s = CH; s < ks; ++s) v += part[(int64_t)s * mn + i];   // ks > CH: K > 16384
+  v *= scale;
   if (p.out_f32)
     ((float *)p.C)[i] = v;
   else
