@@ -158,6 +158,17 @@ def test_w4a8_parity(M, N, K):
     check_both("w4a8", inp, c64, b64, what=f"w4a8 {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M", [1, 40])
+def test_w4a8_parity_long_k(M):
+    """K = 16896 gives 33 split-K partials, one more than the reduction
+    requests up front: the rest of the sum takes its tail loop."""
+    from gpu_cases import check_both, oracle_full
+    N, K = 96, 16896
+    inp = synth.w4a8(M, N, K, seed=M + 3)
+    c64, b64 = oracle_full("w4a8", inp)
+    check_both("w4a8", inp, c64, b64, what=f"w4a8 {M}x{N}x{K}")
+
+
 def test_w4a8_workspace_reuse_across_sizes():
     """One workspace serves a large call then smaller ones (the split-K
     partials it holds need no clearing between calls)."""
