@@ -31,9 +31,10 @@
 //     launch.)
 // Tokens sit on the MFMA's A side, padded to 32: lanes of token rows >= M
 // read row 0 (those MFMA rows are never stored), and only the accumulator
-// registers that hold real tokens are scaled.  Up to 128 tokens go through
-// one launch as up to four 32-token blocks, each weight fragment converted
-// once for all of them; larger M runs in slices of 128.
+// registers that hold real tokens are scaled.  Up to 64 tokens go through
+// one launch as up to two 32-token blocks, each weight fragment converted
+// once for both; more tokens take the tiled kernel (gemm_w4a8_tile.hip),
+// where the per-group FMAs rather than the weight stream are the bound.
 #include "common.h"
 #include "kernels.h"
 
@@ -43,7 +44,8 @@ namespace {
 constexpr int NT = 128;       // weight rows per workgroup (4 waves x 32)
 constexpr int KR = 256;       // K-elements per range
 constexpr int RPW = 2;        // ranges per workgroup, all requested at once
-constexpr int MS = 128;       // tokens per launch (up to 4 blocks of 32)
+constexpr int MS = 64;        // tokens per launch (up to 2 blocks of 32)
+constexpr int TILE_M = 64;    // more tokens than this take the tiled kernel
 
 constexpr int ROWB = KR / 2;          // code bytes per weight row per range
 constexpr int CHUNKS = ROWB / 16;     // 16-byte chunks per code row (2 groups each)
@@ -178,8 +180,8 @@ __device__ __forceinline__ void range_store(Tile<MT> &tile, int M, int klen, int
 // np pairs of 16-element groups (2 groups per code chunk) from the LDS tile
 // QUADS = accumulator quads in use (8 tokens each); 0 means one token: only
 // register 0 (token 0 in the lanes of K-half 0) is updated and stored.  Up to
-// 4 quads fill one 32-token block; QUADS = 8 and 16 are 2 and 4 full blocks
-// (64 and 128 tokens), each code fragment converted once for all blocks.
+// 4 quads fill one 32-token block; QUADS = 8 is 2 full blocks (64 tokens),
+// each code fragment converted once for both.
 template <int QUADS>
 struct Acc {
   static constexpr int MT = QUADS == 0 ? 8 : 8 * QUADS;   // token rows in the LDS tile
@@ -389,15 +391,28 @@ void launch_one(const W4A8Args &p, int ks, float *part, hipStream_t stream) {
 }  // namespace
 
 size_t w4a8_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  const int ks = splits(K);
-  if (ks <= 1) return 0;
-  const int64_t Ms = M < MS ? M : MS;
-  return (size_t)ks * (size_t)Ms * (size_t)N * sizeof(float);
+  int ks = splits(K);
+  if (M > TILE_M) {             // the tiled kernel
+    int gpw;
+    w4a8_tile_split(M, N, K, ks, gpw);
+  }
+  return ks > 1 ? (size_t)ks * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
 
 int64_t w4a8_max_n() { return (int64_t)1 << 30; }
 
 hipError_t launch_w4a8(const W4A8Args &p0, hipStream_t stream) {
+  if (p0.M > TILE_M) {
+    int ks, gpw;
+    w4a8_tile_split(p0.M, p0.N, p0.K, ks, gpw);
+    float *part = ks > 1 ? (float *)p0.work : nullptr;
+    hipError_t e = launch_w4a8_tile(p0, ks, gpw, part, stream);
+    if (e != hipSuccess || ks == 1) return e;
+    const int64_t mn = (int64_t)p0.M * p0.N;
+    hipLaunchKernelGGL(w4a8_splitk_reduce, dim3((unsigned)((mn + 63) / 64)), dim3(64), 0, stream, p0,
+                       ks, part);
+    return hipGetLastError();
+  }
   const int ks = splits(p0.K);
   float *part = ks > 1 ? (float *)p0.work : nullptr;
   for (int m0 = 0; m0 < p0.M; m0 += MS) {
@@ -406,8 +421,7 @@ hipError_t launch_w4a8(const W4A8Args &p0, hipStream_t stream) {
     p.aq = p0.aq + (int64_t)m0 * p0.K;
     p.atok = p0.atok + m0;
     p.C = (char *)p0.C + (int64_t)m0 * p0.N * (p0.out_f32 ? 4 : 2);
-    if (p.M > 64) launch_one<16>(p, ks, part, stream);
-    else if (p.M > 32) launch_one<8>(p, ks, part, stream);
+    if (p.M > 32) launch_one<8>(p, ks, part, stream);
     else if (p.M > 24) launch_one<4>(p, ks, part, stream);
     else if (p.M > 16) launch_one<3>(p, ks, part, stream);
     else if (p.M > 8) launch_one<2>(p, ks, part, stream);

@@ -44,6 +44,9 @@ struct W4A8Args {
 size_t w4a8_workspace_bytes(int64_t M, int64_t N, int64_t K);
 int64_t w4a8_max_n();  // largest N the decode kernel's indexing supports
 hipError_t launch_w4a8(const W4A8Args &p, hipStream_t stream);
+// more than 32 tokens: the tiled kernel (gemm_w4a8_tile.hip) and its K split
+void w4a8_tile_split(int64_t M, int64_t N, int64_t K, int &ks, int &gpw);
+hipError_t launch_w4a8_tile(const W4A8Args &p, int ks, int gpw, float *part, hipStream_t stream);
 
 struct MoeArgs {
   const uint8_t *xq, *xs;

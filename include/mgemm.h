@@ -146,9 +146,10 @@ int mgemm_w4a16(const void *A, const void *Wq, const void *Ws, const float *Sw,
    adds them in split order (results are run-to-run bit-identical).  `ws` is
    device memory of at least mgemm_workspace_bytes(MGEMM_OP_W4A8, M, N, K,
    ...) bytes, 16-byte aligned, with no required contents (when the size is
-   0, ws may be NULL).  Calls that share a workspace must be ordered on one
-   stream.  M is processed in slices of up to 128 rows (one pass over the
-   weight per slice). */
+   0, ws may be NULL); a smaller call does not always need less (more than
+   64 tokens take a tiled kernel with its own K split), so a shared
+   workspace must cover the largest size among its calls.  Calls that share
+   a workspace must be ordered on one stream. */
 int mgemm_w4a8(const void *Aq, const float *a_tok, const void *Wq, const void *Ws,
                const float *Sw, void *C, int64_t M, int64_t N, int64_t K, int out_f32,
                void *ws, size_t ws_bytes, void *stream);
