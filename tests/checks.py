@@ -12,7 +12,9 @@ import numpy as np
 REL_TOL = 1e-5
 
 
-def check_f32(c32, c64, bound, rel=REL_TOL, what=""):
+def check_f32(c32, c64, bound, rel=REL_TOL, what="", extra=None):
+    """extra: an additional absolute allowance per output (the FP8 MFMA
+    summation window, fp8_window_bound), added to rel * bound."""
     c32 = np.asarray(c32, dtype=np.float64).ravel()
     c64 = np.asarray(c64, dtype=np.float64).ravel()
     bound = np.asarray(bound, dtype=np.float64).ravel()
@@ -22,6 +24,10 @@ def check_f32(c32, c64, bound, rel=REL_TOL, what=""):
     assert np.all(np.isfinite(c64)) and np.all(np.isfinite(bound)), f"{what}: non-finite oracle"
     err = np.abs(c32 - c64)
     lim = rel * bound
+    if extra is not None:
+        extra = np.asarray(extra, dtype=np.float64).ravel()
+        assert extra.size == c32.size and np.all(extra >= 0), f"{what}: bad allowance"
+        lim = lim + extra
     bad = np.where((bound == 0) & (c32 != 0) | (err > lim))[0]
     assert bad.size == 0, (f"{what}: {bad.size} of {c32.size} outside 1e-5*B; first at {bad[:5]}: "
                            f"gpu {c32[bad[:5]]} oracle {c64[bad[:5]]} B {bound[bad[:5]]}")
@@ -48,7 +54,7 @@ def check_bf16(bits, ref_bits, what=""):
     return int(d.max())
 
 
-def fp8_window_bound(p):
+def fp8_window_bound(p, gscale=None):
     """Extra error allowance for sums formed by gfx950's FP8 MFMAs.
 
     Measured on the device (one large product plus several tiny ones in one
@@ -60,11 +66,17 @@ def fp8_window_bound(p):
     binades of the group maximum.  Per group the error is thus below
     sum over k of min(|p_k|, 2^(e-13)) for the products with |p_k| < 2^(e-6),
     e = floor(log2(max |p|)).  Returns twice that sum over all groups.
-    p: products [..., K] (FP64, K % 8 == 0, groups aligned to 8)."""
+    p: products [..., K] (FP64, K % 8 == 0, groups aligned to 8) as the MFMA
+    forms them.  gscale: optional factor per group of 8 ([..., K/8]) that is
+    applied to a group's sum after the MFMA (a block scale that is not a power
+    of two), multiplied into that group's bound."""
     a = np.abs(np.asarray(p, dtype=np.float64))
     a = a.reshape(a.shape[:-1] + (a.shape[-1] // 8, 8))
     mx = a.max(axis=-1, keepdims=True)
     e = np.floor(np.log2(np.where(mx > 0, mx, 1.0)))
     q = 2.0 ** (e - 13)
     small = a < 2.0 ** (e - 6)
-    return 2.0 * (np.minimum(a, q) * small).sum(axis=(-1, -2))
+    g = (np.minimum(a, q) * small).sum(axis=-1)
+    if gscale is not None:
+        g = g * np.abs(np.asarray(gscale, dtype=np.float64))
+    return 2.0 * g.sum(axis=-1)

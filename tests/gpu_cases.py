@@ -8,7 +8,7 @@ import block_scaled_precision_tn_amd as mg
 import oracle
 from oracle import BF16, FP8TOK, MXFP8, NVFP4, Operand
 
-from checks import check_bf16, check_f32
+from checks import check_bf16, check_f32, fp8_window_bound
 
 
 def dev(a, dtype=None):
@@ -97,15 +97,53 @@ def oracle_points(fmt, inp, m, n):
     return oracle.gemm_points(A, W, m, n)
 
 
+def w4a8_window(inp, m=None, n=None):
+    """FP8 MFMA summation-window allowance (fp8_window_bound) of each W4A8
+    output, everywhere [M,N] or at the points (m[i], n[i]).  The MFMA forms
+    the products of the E4M3 token values with the E2M1 weight values (the
+    power-of-two factor of the E2M1 -> E4M3 route changes nothing); a group's
+    E4M3 weight scale, the token factor and the tensor scale multiply its sum
+    afterwards."""
+    e4 = np.array([oracle.dec_e4m3(b) for b in range(256)])
+    e2 = np.array([oracle.dec_e2m1(c) for c in range(16)])
+    aq, wq, ws = inp["aq"], inp["wq"], inp["ws"]
+    M, N = aq.shape[0], wq.shape[0]
+    rf = np.asarray(inp["atok"], dtype=np.float64).ravel() * float(np.ravel(inp["Sw"])[0])
+
+    def wvals(rows):                     # E2M1 values [rows, K], group scales [rows, K/8]
+        q = wq[rows].astype(np.int64)
+        codes = np.empty((q.shape[0], 2 * q.shape[1]), np.int64)
+        codes[:, 0::2] = q & 15
+        codes[:, 1::2] = q >> 4
+        return e2[codes], np.repeat(e4[ws[rows].astype(np.int64)], 2, axis=1)
+
+    if m is None:
+        wv, gs = wvals(np.arange(N))
+        out = np.empty((M, N))
+        for i in range(M):
+            out[i] = fp8_window_bound(e4[aq[i].astype(np.int64)][None, :] * wv, gs) * rf[i]
+        return out
+    m, n = np.asarray(m).ravel(), np.asarray(n).ravel()
+    out = np.empty(m.size)
+    for s in range(0, m.size, 256):
+        mi, ni = m[s:s + 256], n[s:s + 256]
+        wv, gs = wvals(ni)
+        out[s:s + 256] = fp8_window_bound(e4[aq[mi].astype(np.int64)] * wv, gs) * rf[mi]
+    return out
+
+
 def check_both(fmt, inp, c64, b64, m=None, n=None, what=""):
     """Run the GPU path in FP32 and BF16 output modes and compare both with
-    the oracle (at the given points, or everywhere).  Returns max err/B."""
+    the oracle (at the given points, or everywhere).  W4A8 sums on the FP8
+    MFMA, so its tolerance adds that instruction's summation-window
+    allowance.  Returns max err/B."""
     g32 = GPU[fmt](inp, True)
     g16 = GPU[fmt](inp, False)
     if m is not None:
         g32, g16 = g32[m, n], g16[m, n]
-    rel = check_f32(g32, c64, b64, what=what + " fp32")
-    check_bf16_vs(g16, c64, b64, what=what + " bf16")
+    extra = w4a8_window(inp, m, n) if fmt == "w4a8" else None
+    rel = check_f32(g32, c64, b64, what=what + " fp32", extra=extra)
+    check_bf16_vs(g16, c64, b64, what=what + " bf16", extra=extra)
     return rel, g32, g16
 
 

@@ -150,7 +150,8 @@ def test_w4a16_parity(M, N, K):
 @pytest.mark.parametrize("M", [1, 3, 8, 17, 32, 33, 100, 128, 200])
 @pytest.mark.parametrize("N,K", [(96, 256), (200, 1024), (384, 2048),
                                  (130, 1536),    # odd number of 512-element K ranges
-                                 (257, 1568)])   # partial last range, K/16 not a multiple of 16
+                                 (257, 1568),    # partial last range, K/16 not a multiple of 16
+                                 (96, 64)])      # one stage of K: no split (tiled path for M > 64)
 def test_w4a8_parity(M, N, K):
     from gpu_cases import check_both, oracle_full
     inp = synth.w4a8(M, N, K, seed=M + N)
