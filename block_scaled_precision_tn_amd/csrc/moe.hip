@@ -506,22 +506,282 @@ __global__ __launch_bounds__(256) void k_down(MoeArgs p, const int32_t *meta, co
     }
 }
 
-// one thread per (token, 4 columns): slots summed in order 0..topk-1
+// ------------------------------------------- decode-sized MoE (swap-AB)
+// With few tokens each expert holds at most a few routed rows, and the call
+// streams the active experts' weights once: it is bound by HBM, not by the
+// matrix unit.  These two kernels put the weight rows on the MFMA's A side
+// (64 per workgroup: two 32-row blocks) and an expert's routed rows (up to 32,
+// one block; more are taken 32 at a time) on the B side, each workgroup
+// covering the whole of K, so the grids have many workgroups per active
+// expert.  Operands go straight from global memory into an LDS ring of SL
+// slots (stages of 128 K-elements: 8 KB of weight codes, 4 KB of token codes
+// and the rows' E8M0 scale bytes), SL - 1 stages in flight: 6 slots (two
+// workgroups per CU) when the grid has at most two workgroups per CU, else 4
+// (three per CU, more stages in flight per CU).  Each of the 4 waves
+// computes one (block, K-step) pair of every stage; the two waves of a block
+// add their sums in a fixed order at the end.
+//   k_dec<true>  gate/up: rows [i0, i0+32) of the gate and of the up half of
+//                w13[e]; epilogue: GLU and MXFP8 re-quantisation of the 32
+//                h columns (one scale block) of each routed row
+//   k_dec<false> down: rows [n0, n0+64) of w2[e]; epilogue: times the
+//                routing weight, FP32 rows as k_down stores them
+constexpr int DROWS = 64;              // weight rows per workgroup
+constexpr int DKS = 128;               // K per stage
+constexpr int DWB = DROWS * DKS;       // weight code bytes per stage
+constexpr int DXB = 32 * DKS;          // token code bytes per stage
+constexpr int DSB = 256 * 4;           // scale bytes per stage: one dword per lane of the workgroup
+constexpr int DLOADS = 4;              // direct loads per lane per stage
+
+// chunk `chunk` (16 bytes) of 128-byte stage row `row`, XOR-ed with (row / 2) % 8
+// so the 16 rows one MFMA fragment read touches at a chunk index cover all
+// 64 LDS banks
+__device__ __forceinline__ int dk_off(int row, int chunk) {
+  return row * DKS + ((chunk ^ ((row >> 1) & 7)) << 4);
+}
+
+template <bool GU, int DSLOT>
+__global__ __launch_bounds__(256) void k_dec(MoeArgs p, const int32_t *meta, const int32_t *sorted,
+                                             const float *wsorted, const int32_t *tile_e,
+                                             const int32_t *tile_r, const int32_t *tile_n,
+                                             uint8_t *hq, uint8_t *hs, float *y) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lw[DSLOT * DWB];
+  __shared__ __attribute__((aligned(1024))) uint8_t lx[DSLOT * DXB];
+  __shared__ __attribute__((aligned(1024))) uint8_t ls[DSLOT * DSB];
+  const int tile = blockIdx.y;
+  if (tile >= meta[0]) return;
+  const int e = tile_e[tile], r0 = tile_r[tile], nrows = tile_n[tile];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int H = p.H, I = p.I, K = GU ? H : I, KB = K / 32;
+  const int c0 = blockIdx.x * (GU ? 32 : DROWS);   // first h column (gate/up) or hidden column (down)
+  const int kstep = wave & 1, blk = wave >> 1;     // this wave's K-step of a stage and weight block
+
+  // weight row q (0..63) of this workgroup, as a row index of w13[e] / w2[e]
+  auto wrow = [&](int q) -> int64_t {
+    if (GU) return (int64_t)e * 2 * I + (q < 32 ? c0 + q : I + c0 + q - 32);
+    return (int64_t)e * H + (c0 + q < H ? c0 + q : H - 1);
+  };
+  const uint8_t *wq = GU ? p.w13q : p.w2q, *wsc = GU ? p.w13s : p.w2s;
+  const uint8_t *xq = GU ? p.xq : hq, *xsc = GU ? p.xs : hs;
+
+  for (int tb = 0; tb < nrows; tb += 32) {
+    const int nt = nrows - tb < 32 ? nrows - tb : 32;
+    // token (gate/up) or sorted h row (down) of routed row tb + t; rows past
+    // the block repeat its first row (their outputs are never stored)
+    auto xrow = [&](int t) -> int64_t {
+      const int rr = r0 + tb + (t < nt ? t : 0);
+      return GU ? (int64_t)(sorted[rr] / p.topk) : (int64_t)rr;
+    };
+    // this lane's direct loads of a stage: 2 weight chunks, 1 token chunk
+    // (16 bytes each; 8 lanes per 128-byte stage row) and one scale dword
+    const uint8_t *gw[2], *gx;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int row = 16 * wave + 8 * j + (lane >> 3);
+      gw[j] = wq + wrow(row) * K + 16 * ((lane & 7) ^ ((row >> 1) & 7));
+    }
+    {
+      const int row = 8 * wave + (lane >> 3);
+      gx = xq + xrow(row) * K + 16 * ((lane & 7) ^ ((row >> 1) & 7));
+    }
+    // scale dword of the stage: lanes 0..63 weight rows, 64..95 token rows,
+    // the rest repeat weight row 0 (never read)
+    const uint8_t *gs = tid < 64 ? wsc + wrow(tid) * KB : (tid < 96 ? xsc + xrow(tid - 64) * KB : wsc + wrow(0) * KB);
+    auto issue = [&](int s, int slot) {
+      const int k0 = s * DKS;
+      dma16(gw[0] + k0, lw + slot * DWB + 1024 * (2 * wave));
+      dma16(gw[1] + k0, lw + slot * DWB + 1024 * (2 * wave + 1));
+      dma16(gx + k0, lx + slot * DXB + 1024 * wave);
+      dma4(gs + k0 / 32, ls + slot * DSB + 256 * wave);
+    };
+
+    f32x16 acc = {0};
+    const int S = K / DKS;
+#pragma unroll
+    for (int j = 0; j < DSLOT - 1; ++j) issue(j < S ? j : S - 1, j);
+    for (int s = 0, slot = 0; s < S; ++s, slot = slot == DSLOT - 1 ? 0 : slot + 1) {
+      __builtin_amdgcn_sched_barrier(0);
+      // stage s has landed once at most the loads of the DSLOT - 2 stages
+      // after it are outstanding (stages past the end reload the last one:
+      // never computed)
+      wait_vmcnt<(DSLOT - 2) * DLOADS>();
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      // stage s + DSLOT - 1 into the slot stage s - 1 used (every wave is past it)
+      issue(s + DSLOT - 1 < S ? s + DSLOT - 1 : S - 1, slot == 0 ? DSLOT - 1 : slot - 1);
+      const uint8_t *aw = lw + slot * DWB, *ax = lx + slot * DXB, *as = ls + slot * DSB;
+      const int arow = 32 * blk + l32;
+      const u32x4 alo = *(const u32x4 *)(aw + dk_off(arow, 4 * kstep + h));
+      const u32x4 ahi = *(const u32x4 *)(aw + dk_off(arow, 4 * kstep + 2 + h));
+      const u32x4 blo = *(const u32x4 *)(ax + dk_off(l32, 4 * kstep + h));
+      const u32x4 bhi = *(const u32x4 *)(ax + dk_off(l32, 4 * kstep + 2 + h));
+      // scale of 32-element block (2 kstep + h) of the stage: lane (row, h) of
+      // each operand supplies block h of its row
+      const int sa = as[4 * arow + 2 * kstep + h], sb = as[4 * (64 + l32) + 2 * kstep + h];
+      const i32x8 fa = {(int)alo[0], (int)alo[1], (int)alo[2], (int)alo[3], (int)ahi[0], (int)ahi[1], (int)ahi[2], (int)ahi[3]};
+      const i32x8 fb = {(int)blo[0], (int)blo[1], (int)blo[2], (int)blo[3], (int)bhi[0], (int)bhi[1], (int)bhi[2], (int)bhi[3]};
+      acc = mfma_mx_fp8(fa, fb, acc, sa, sb);
+    }
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+
+    // block sums: wave 2b + 1's partial added to wave 2b's (K-steps 0 then 1);
+    // for gate/up the up block (wave 2) is then handed to wave 0
+    float *red = (float *)lw;   // [wave][register][lane]
+    if (kstep == 1) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) red[(wave * 16 + r) * 64 + lane] = acc[r];
+    }
+    __syncthreads();
+    if (kstep == 0) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] += red[((wave + 1) * 16 + r) * 64 + lane];
+    }
+    const int t = l32;                 // routed row (token column) of this lane
+    if (GU) {
+      __syncthreads();
+      if (wave == 2) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) red[(1 * 16 + r) * 64 + lane] = acc[r];
+      }
+      __syncthreads();
+      if (wave == 0) {
+        // h = silu(g) * u for columns c0 + row(r) of routed row t; its MXFP8
+        // block of 32 columns is this lane's 16 values and lane ^ 32's
+        float hv[16];
+        float amax = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float g = acc[r], u = red[(1 * 16 + r) * 64 + lane];
+          hv[r] = (g / (1.0f + expf(-g))) * u;
+          amax = fmaxf(amax, fabsf(hv[r]));
+        }
+        amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+        uint32_t sbyte = 0u;
+        int X = 0;
+        if (amax != 0.0f) {
+          X = (int)((__builtin_bit_cast(uint32_t, amax) >> 23) & 0xFF) - 127 - 8;
+          X = X < -127 ? -127 : (X > 127 ? 127 : X);
+          sbyte = (uint32_t)(X + 127);
+        }
+        if (t < nt) {
+          const int64_t srow = r0 + tb + t;
+          uint8_t *dq = hq + srow * I + c0;
+          uint8_t *dd = p.dbg_h ? p.dbg_h + (int64_t)sorted[srow] * (I + I / 32) : nullptr;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {   // registers 4q..4q+3: columns 8q + 4h + 0..3
+            uint32_t w4 = 0u;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+              const uint32_t code = amax == 0.0f ? 0u : f32_to_e4m3_rne_sat(__builtin_ldexpf(hv[4 * q + b], -X));
+              w4 |= code << (8 * b);
+            }
+            *(uint32_t *)(dq + 8 * q + 4 * h) = w4;
+            if (dd) *(uint32_t *)(dd + c0 + 8 * q + 4 * h) = w4;
+          }
+          if (h == 0) {
+            hs[srow * (I / 32) + c0 / 32] = (uint8_t)sbyte;
+            if (dd) dd[I + c0 / 32] = (uint8_t)sbyte;
+          }
+        }
+      }
+    } else if (kstep == 0 && t < nt) {
+      // rows c0 + 32 blk + row(r) of y for routed row t, times its routing weight
+      const int64_t srow = r0 + tb + t;
+      const float w = wsorted[srow];
+      float *yrow = y + srow * H + c0 + 32 * blk;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = 8 * q + 4 * h;
+        if (c0 + 32 * blk + n < H)
+          *(f32x4 *)(yrow + n) = f32x4{acc[4 * q] * w, acc[4 * q + 1] * w, acc[4 * q + 2] * w, acc[4 * q + 3] * w};
+      }
+    }
+    // the ring (and the reduction area inside it) is reused by the next block
+    __syncthreads();
+  }
+}
+
+// one thread per (token, 4 columns): slots summed in order 0..topk-1; every
+// slot's row index, then every row, is requested before the first add
 __global__ void k_combine(const float *y, const int32_t *pos, int T, int H, int topk,
                           uint16_t *out) {
+  constexpr int MAXK = 16;   // topk limit of the entry point
   const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t per_t = H / 4;
   if (q >= (int64_t)T * per_t) return;
   const int t = (int)(q / per_t), c = (int)(q % per_t) * 4;
+  int r[MAXK];
+#pragma unroll
+  for (int j = 0; j < MAXK; ++j) r[j] = j < topk ? pos[(int64_t)t * topk + j] : -1;
+  f32x4 v[MAXK];
+#pragma unroll
+  for (int j = 0; j < MAXK; ++j)
+    v[j] = r[j] >= 0 ? *(const f32x4 *)(y + (int64_t)r[j] * H + c) : f32x4{0, 0, 0, 0};
   f32x4 a = {0, 0, 0, 0};
-  for (int j = 0; j < topk; ++j) {
-    const int r = pos[(int64_t)t * topk + j];
-    if (r >= 0) a += *(const f32x4 *)(y + (int64_t)r * H + c);
-  }
+#pragma unroll
+  for (int j = 0; j < MAXK; ++j) a = r[j] >= 0 ? a + v[j] : a;
   *(u32x2 *)(out + (int64_t)t * H + c) = u32x2{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
 }
 
+// Decode-sized routing (R <= 1024 entries, E <= 1024 experts) in one
+// workgroup: what k_prep, k_count, k_scan and k_scatter do, with the expert
+// counters and both scans in LDS, so the call spends one launch on it.
+__global__ __launch_bounds__(1024) void k_route_small(const int32_t *ids, const float *tw, int R,
+                                                      int E, int32_t *offs, int32_t *meta,
+                                                      int32_t *tile_e, int32_t *tile_r,
+                                                      int32_t *tile_n, int32_t *pos,
+                                                      int32_t *sorted, float *wsorted) {
+  __shared__ uint32_t s_cnt[1024];
+  __shared__ int s_rows[1024], s_tiles[1024];
+  const int tid = threadIdx.x;
+  s_cnt[tid] = 0u;
+  __syncthreads();
+  const int e = tid < R ? ids[tid] : -1;
+  const bool ok = e >= 0 && e < E;
+  const uint32_t rk = ok ? atomicAdd(&s_cnt[e], 1u) : 0u;   // rank within the expert
+  __syncthreads();
+  // inclusive scans over experts (thread = expert) of rows and 128-row tiles
+  const int c = tid < E ? (int)s_cnt[tid] : 0, nt = (c + BM - 1) / BM;
+  s_rows[tid] = c;
+  s_tiles[tid] = nt;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int ar = tid >= o ? s_rows[tid - o] : 0, at = tid >= o ? s_tiles[tid - o] : 0;
+    __syncthreads();
+    s_rows[tid] += ar;
+    s_tiles[tid] += at;
+    __syncthreads();
+  }
+  if (tid == 1023) meta[0] = s_tiles[1023];
+  if (tid < E) {
+    const int rb = s_rows[tid] - c, tb = s_tiles[tid] - nt;
+    offs[tid] = rb;
+    for (int q = 0; q < nt; ++q) {
+      tile_e[tb + q] = tid;
+      tile_r[tb + q] = rb + q * BM;
+      tile_n[tb + q] = c - q * BM < BM ? c - q * BM : BM;
+    }
+  }
+  if (tid < R) {
+    if (ok) {
+      const int p = s_rows[e] - (int)s_cnt[e] + (int)rk;
+      pos[tid] = p;
+      sorted[p] = tid;
+      wsorted[p] = tw[tid];
+    } else {
+      pos[tid] = -1;
+    }
+  }
+}
+
 }  // namespace
+
+// the decode-sized kernels serve up to 32 tokens when both K dimensions are
+// whole stages (an expert then has at most 32 rows unless a token names it
+// twice; such rows are taken 32 at a time)
+static bool dec_path(const MoeArgs &p) {
+  return p.T <= 32 && (int64_t)p.T * p.topk <= 1024 && p.H % DKS == 0 && p.I % DKS == 0;
+}
 
 size_t moe_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk) {
   return layout(T, H, I, E, topk).total;
@@ -543,13 +803,38 @@ hipError_t launch_moe(const MoeArgs &p, hipStream_t stream) {
   const int64_t TH4 = (int64_t)p.T * (p.H / 4);
 
   int32_t *offs = (int32_t *)(w + L.offs);
+  float *wsorted = (float *)(w + L.wsorted);
+  if (dec_path(p)) {
+    // decode-sized: one routing launch; every active tile has at least one
+    // row, so at most R tiles
+    hipLaunchKernelGGL(k_route_small, dim3(1), dim3(1024), 0, stream, p.ids, p.tw, L.R, p.E, offs,
+                       meta, tile_e, tile_r, tile_n, pos, sorted, wsorted);
+    const unsigned ty = (unsigned)(L.maxtiles < L.R ? L.maxtiles : L.R);
+    const dim3 gg(p.I / 32, ty), gd(p.H / DROWS, ty);
+    // at most two active workgroups per CU (of 256): the deeper ring
+    const int64_t te = p.E < L.R ? p.E : L.R;   // active tiles, without repeated experts
+    if (te * (p.I / 32) <= 512)
+      hipLaunchKernelGGL((k_dec<true, 6>), gg, dim3(256), 0, stream, p, meta, sorted, wsorted,
+                         tile_e, tile_r, tile_n, hq, hs, y);
+    else
+      hipLaunchKernelGGL((k_dec<true, 4>), gg, dim3(256), 0, stream, p, meta, sorted, wsorted,
+                         tile_e, tile_r, tile_n, hq, hs, y);
+    if (te * (p.H / DROWS) <= 512)
+      hipLaunchKernelGGL((k_dec<false, 6>), gd, dim3(256), 0, stream, p, meta, sorted, wsorted,
+                         tile_e, tile_r, tile_n, hq, hs, y);
+    else
+      hipLaunchKernelGGL((k_dec<false, 4>), gd, dim3(256), 0, stream, p, meta, sorted, wsorted,
+                         tile_e, tile_r, tile_n, hq, hs, y);
+    hipLaunchKernelGGL(k_combine, dim3((unsigned)((TH4 + 255) / 256)), dim3(256), 0, stream, y,
+                       pos, p.T, p.H, p.topk, p.out);
+    return hipGetLastError();
+  }
   const int rb = (L.R + 255) / 256;
   hipLaunchKernelGGL(k_prep, dim3((p.E + 255) / 256), dim3(256), 0, stream, counts, p.E);
   hipLaunchKernelGGL(k_count, dim3((L.R + 1023) / 1024), dim3(1024), 0, stream, p.ids, L.R, p.E,
                      counts, pos);
   hipLaunchKernelGGL(k_scan, dim3(1), dim3(256), 0, stream, counts, p.E, offs, meta, tile_e,
                      tile_r, tile_n);
-  float *wsorted = (float *)(w + L.wsorted);
   hipLaunchKernelGGL(k_scatter, dim3(rb), dim3(256), 0, stream, p.ids, p.tw, L.R, offs, pos, sorted,
                      wsorted);
   // scale rows of 16-byte multiples (K % 512 == 0) take the chunked scale loads

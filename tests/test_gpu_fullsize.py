@@ -75,3 +75,16 @@ def test_moe_full_size_sampled_tokens():
     nd = _check_requant(inp, d, T, H, I, topk, tokens=tokens)
     assert nd <= max(4, len(tokens) * topk * I // 100), nd
     _check_down_combine(inp, d, out, T, H, I, topk, tokens)
+
+
+@pytest.mark.parametrize("T", [1, 16])
+def test_moe_decode_full_size(T):
+    """Decode-sized token counts at the full MoE shape (the swap-AB kernels)."""
+    from test_gpu_moe import _check_down_combine, _check_requant, run_moe
+    H, I, E, topk = 4096, 1536, 64, 8
+    inp = synth.moe(T, H, I, E, topk, seed=T)
+    out, d = run_moe(inp, T, H, I, E, topk)
+    tokens = np.arange(T) if T <= 4 else np.array([0, 5, T - 1])
+    nd = _check_requant(inp, d, T, H, I, topk, tokens=tokens)
+    assert nd <= max(4, len(tokens) * topk * I // 100), nd
+    _check_down_combine(inp, d, out, T, H, I, topk, tokens)

@@ -152,11 +152,15 @@ def _check_down_combine(inp, d, out, T, H, I, topk, tokens):
     check_bf16_vs(out[tokens], ref, bnd, what="moe out", extra=extra)
 
 
-# H or I a multiple of 512 takes the chunked scale loads (16 bytes of a scale
-# row per lane for 8 stages); the others the per-stage 2-byte loads
+# More than 32 tokens take the grouped kernels: H or I a multiple of 512
+# takes the chunked scale loads (16 bytes of a scale row per lane for 8
+# stages), the others the per-stage 2-byte loads.  Up to 32 tokens with H and
+# I multiples of 128 take the decode-sized (swap-AB) kernels.
 @pytest.mark.parametrize("T,H,I,E,topk", [(64, 256, 128, 8, 4), (300, 128, 192, 6, 3),
                                           (33, 64, 64, 16, 2), (40, 1024, 512, 4, 2),
-                                          (24, 512, 1536, 3, 2)])
+                                          (24, 512, 1536, 3, 2), (1, 512, 256, 8, 4),
+                                          (7, 256, 384, 16, 3), (32, 1024, 512, 8, 2),
+                                          (16, 128, 128, 64, 8), (5, 64, 128, 4, 2)])
 def test_moe_stagewise(T, H, I, E, topk):
     inp = synth.moe(T, H, I, E, topk, seed=T + E)
     out, d = run_moe(inp, T, H, I, E, topk)
@@ -176,6 +180,50 @@ def test_moe_skewed_routing_and_empty_experts():
     out, d = run_moe(inp, T, H, I, E, topk)
     _check_requant(inp, d, T, H, I, topk)
     _check_down_combine(inp, d, out, T, H, I, topk, np.arange(T))
+
+
+def test_moe_hand_case_decode_kernels():
+    """The hand case at H = I = 128 (one token: the decode-sized kernels)."""
+    g = json.load(open(os.path.join(GOLD, "moe_hand_128.json")))
+    H, I = g["H"], g["I"]
+    inp = dict(
+        xq=np.full((1, H), int(g["x_code"], 16), np.uint8),
+        xs=np.full((1, H // 32), g["x_scale"], np.uint8),
+        w13q=np.concatenate([np.full((1, I, H), int(g["gate_code"], 16), np.uint8),
+                             np.full((1, I, H), int(g["up_code"], 16), np.uint8)], axis=1),
+        w13s=np.full((1, 2 * I, H // 32), g["w13_scale"], np.uint8),
+        w2q=np.full((1, H, I), int(g["w2_code"], 16), np.uint8),
+        w2s=np.full((1, H, I // 32), g["w2_scale"], np.uint8),
+        ids=np.zeros((1, 1), np.int32), tw=np.ones((1, 1), np.float32))
+    out, d = run_moe(inp, 1, H, I, 1, 1)
+    assert np.all(d[0, :I] == int(g["h_code"], 16)) and np.all(d[0, I:] == g["h_scale"])
+    assert np.all(out == int(g["out_bf16"], 16))
+    o64, _ = oracle.moe_tokens(inp, 1, H, I, 1, 1, [0])
+    assert np.all(o64 == g["out"])
+
+
+def test_moe_decode_expert_named_twice():
+    """Few tokens, each naming expert 0 in two slots: expert 0 gets more than
+    32 rows, which the decode-sized kernels take 32 at a time."""
+    T, H, I, E, topk = 20, 256, 256, 4, 4
+    inp = synth.moe(T, H, I, E, topk, seed=11)
+    ids = np.zeros((T, topk), np.int32)
+    ids[:, 2] = 1 + np.arange(T) % 3
+    ids[:, 3] = np.arange(T) % 4
+    inp["ids"] = ids
+    out, d = run_moe(inp, T, H, I, E, topk)
+    _check_requant(inp, d, T, H, I, topk)
+    _check_down_combine(inp, d, out, T, H, I, topk, np.arange(T))
+
+
+@pytest.mark.parametrize("T", [3, 32])
+def test_moe_decode_repeat_bit_identical(T):
+    H, I, E, topk = 256, 256, 8, 4
+    inp = synth.moe(T, H, I, E, topk, seed=12)
+    o1, d1 = run_moe(inp, T, H, I, E, topk)
+    o2, d2 = run_moe(inp, T, H, I, E, topk)
+    assert np.array_equal(d1, d2)
+    assert np.array_equal(o1, o2)
 
 
 def test_moe_repeat_bit_identical():
