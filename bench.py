@@ -43,7 +43,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quick", action="store_true", help="headline kernel only")
-    ap.add_argument("--only", default="", help="w4a4|w4a8|bf16|moe (profiling runs)")
+    ap.add_argument("--only", default="", help="w4a4|w4a8|bf16|moe|moe_decode (profiling runs)")
+    ap.add_argument("--moe-dec-tokens", default="1,16",
+                    help="token counts of the decode-sized MoE calls")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run one plain copy kernel of this many MiB (counter calibration)")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -245,7 +247,7 @@ def main():
         torch.cuda.empty_cache()
 
     # ------------------------------------------------------------------- MoE
-    if args.only in ("", "moe") and not args.quick:
+    if args.only in ("", "moe", "moe_decode") and not args.quick:
         T, H, I, E, topk = 4096, 4096, 1536, 64, 8
         m = synth.moe(T, H, I, E, topk, seed=0)
         dm = {k: todev(v) for k, v in m.items()}
@@ -253,11 +255,31 @@ def main():
         wsp = mg.workspace(mg.mgemm_workspace_bytes(mg.OP_MOE, T=T, H=H, I=I, E=E, topk=topk), "moe")
         call = lambda i: mg.mgemm_moe_mxfp8_glu(dm["xq"], dm["xs"], dm["ids"], dm["tw"], dm["w13q"],  # noqa: E731
                                                 dm["w13s"], dm["w2q"], dm["w2s"], o, ws=wsp)
-        ms = timed(torch, call, max(3, args.steps // 2), min(args.warmup, 10), stream)
-        fl = 2.0 * T * topk * (H * 2 * I + I * H)
-        tf = fl / (ms * 1e-3) / 1e12
-        out["moe"] = {"T": T, "H": H, "I": I, "E": E, "topk": topk, "ms": round(ms, 3),
-                      "tflops": round(tf, 1), "frac_fp8_peak": round(tf / PEAK["fp8"], 4)}
+        if args.only != "moe_decode":
+            ms = timed(torch, call, max(3, args.steps // 2), min(args.warmup, 10), stream)
+            fl = 2.0 * T * topk * (H * 2 * I + I * H)
+            tf = fl / (ms * 1e-3) / 1e12
+            out["moe"] = {"T": T, "H": H, "I": I, "E": E, "topk": topk, "ms": round(ms, 3),
+                          "tflops": round(tf, 1), "frac_fp8_peak": round(tf / PEAK["fp8"], 4)}
+        # decode-sized calls (the swap-AB kernels): the first Td tokens of the
+        # same inputs; the call streams the weights of the experts they name
+        dec = []
+        for Td in [int(v) for v in args.moe_dec_tokens.split(",") if v] if args.only != "moe" else []:
+            sl = {k: dm[k][:Td].contiguous() for k in ("xq", "xs", "ids", "tw")}
+            od = torch.empty((Td, H), dtype=torch.bfloat16, device=dev)
+            wsd = mg.workspace(mg.mgemm_workspace_bytes(mg.OP_MOE, T=Td, H=H, I=I, E=E, topk=topk),
+                               "moe_dec")
+            calld = lambda i, sl=sl, od=od, wsd=wsd: mg.mgemm_moe_mxfp8_glu(  # noqa: E731
+                sl["xq"], sl["xs"], sl["ids"], sl["tw"], dm["w13q"], dm["w13s"], dm["w2q"],
+                dm["w2s"], od, ws=wsd)
+            us = timed(torch, calld, max(20, args.steps), min(args.warmup, 20), stream) * 1e3
+            ne = len(np.unique(m["ids"][:Td]))
+            nbytes = (ne * 3 * I * H * (1 + 1 / 32)                  # expert weights, codes + scales
+                      + Td * H * (1 + 1 / 32) + Td * topk * 8 + 2 * Td * H)   # x, routing, out
+            dec.append({"T": Td, "experts": ne, "us": round(us, 2), "bytes": int(nbytes),
+                        "GBps": round(nbytes / us / 1e3, 1),
+                        "frac_hbm": round(nbytes / us / 1e3 / PEAK["hbm"], 4)})
+        out["moe_decode"] = dec
         del dm, o
         torch.cuda.empty_cache()
 
@@ -323,6 +345,7 @@ def main():
         "decode": out.get("decode"),
         "bf16": out.get("bf16"),
         "moe": out.get("moe"),
+        "moe_decode": out.get("moe_decode"),
         "device": torch.cuda.get_device_properties(0).gcnArchName,
         "kernel_src": src_hash("gemm_w4a4.hip", "common.h"),
     }

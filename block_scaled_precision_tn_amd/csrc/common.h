@@ -165,11 +165,6 @@ __device__ __forceinline__ void dma2(const void *g, const void *lds) {
                "s"(lds_addr(lds))
                : "memory", "m0");
 }
-__device__ __forceinline__ void dma4(const void *g, const void *lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g),
-               "s"(lds_addr(lds))
-               : "memory", "m0");
-}
 
 // row held by accumulator register r of lane l (see the layout note above)
 __device__ __forceinline__ int acc_row(int r, int lane) {

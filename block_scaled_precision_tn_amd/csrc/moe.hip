@@ -525,6 +525,14 @@ __global__ __launch_bounds__(256) void k_down(MoeArgs p, const int32_t *meta, co
 //                h columns (one scale block) of each routed row
 //   k_dec<false> down: rows [n0, n0+64) of w2[e]; epilogue: times the
 //                routing weight, FP32 rows as k_down stores them
+// direct-to-LDS load of one dword per lane (lane i at lds + 4 i), tracked by
+// the kernel's own vmcnt waits like dma16
+__device__ __forceinline__ void dma4(const void *g, const void *lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g),
+               "s"(lds_addr(lds))
+               : "memory", "m0");
+}
+
 constexpr int DROWS = 64;              // weight rows per workgroup
 constexpr int DKS = 128;               // K per stage
 constexpr int DWB = DROWS * DKS;       // weight code bytes per stage
