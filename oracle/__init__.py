@@ -78,6 +78,23 @@ def _load():
     lib.orc_moe_tokens.restype = C.c_int
     lib.orc_moe_tokens.argtypes = [C.c_void_p] * 4 + [i64] * 5 + [C.c_void_p] * 5 + [i64] + \
         [C.c_void_p, C.c_void_p, C.c_int]
+    f32 = C.c_float
+    lib.orc_enc_e2m1_rne_sat.restype = C.c_uint8
+    lib.orc_enc_e2m1_rne_sat.argtypes = [f32]
+    lib.orc_nvq.restype = None
+    lib.orc_nvq.argtypes = [C.c_void_p, i64, f32, C.c_void_p, C.c_void_p]
+    lib.orc_moe4_gateup.restype = None
+    lib.orc_moe4_gateup.argtypes = [C.c_void_p, C.c_void_p, f32, i64, i64, C.c_void_p,
+                                    C.c_void_p, C.c_void_p, i64, i64] + [C.c_void_p] * 4
+    lib.orc_moe4_glu_requant.restype = None
+    lib.orc_moe4_glu_requant.argtypes = [C.c_void_p, C.c_void_p, i64, f32, C.c_void_p,
+                                         C.c_void_p]
+    lib.orc_moe4_down.restype = None
+    lib.orc_moe4_down.argtypes = [C.c_void_p, C.c_void_p, f32, i64, C.c_void_p, C.c_void_p,
+                                  C.c_void_p, i64, i64, C.c_void_p, C.c_void_p]
+    lib.orc_moe4_tokens.restype = C.c_int
+    lib.orc_moe4_tokens.argtypes = [C.c_void_p, C.c_void_p, f32, C.c_void_p, C.c_void_p] + \
+        [i64] * 5 + [C.c_void_p] * 6 + [f32, C.c_void_p, i64, C.c_void_p, C.c_void_p, C.c_int]
     _lib = lib
     return lib
 
@@ -282,4 +299,70 @@ def moe_tokens(inp: dict, T, H, I, E, topk, tokens, nthreads=None):
                                 bound.ctypes.data, _nthreads(nthreads))
     if rc != 0:
         raise ValueError("oracle: bad moe arguments")
+    return out, bound
+
+
+# ------------------------------------------------------------ NVFP4 MoE
+def enc_e2m1(v: float) -> int:
+    return _load().orc_enc_e2m1_rne_sat(float(v))
+
+
+def nvq(v, S):
+    """NVFP4 quantisation taken in FP32 under tensor scale S: (codes [n/2], scales [n/16])."""
+    v = np.ascontiguousarray(v, dtype=np.float32).ravel()
+    codes = np.zeros(v.size // 2, np.uint8)
+    scales = np.zeros(v.size // 16, np.uint8)
+    _load().orc_nvq(v.ctypes.data, v.size, float(S), codes.ctypes.data, scales.ctypes.data)
+    return codes, scales
+
+
+def moe4_gateup(inp, t, e, H, I):
+    g, u, bg, bu = (np.zeros(I) for _ in range(4))
+    a = {k: np.ascontiguousarray(inp[k]) for k in ("xq", "xs", "w13q", "w13s", "Sw13")}
+    _load().orc_moe4_gateup(a["xq"].ctypes.data, a["xs"].ctypes.data, float(inp["Sx"]), t, e,
+                            a["w13q"].ctypes.data, a["w13s"].ctypes.data,
+                            np.ascontiguousarray(a["Sw13"], np.float32).ctypes.data, H, I,
+                            g.ctypes.data, u.ctypes.data, bg.ctypes.data, bu.ctypes.data)
+    return g, u, bg, bu
+
+
+def moe4_glu_requant(g, u, Sh):
+    g = np.ascontiguousarray(g, dtype=np.float64)
+    u = np.ascontiguousarray(u, dtype=np.float64)
+    I = g.size
+    hq = np.zeros(I // 2, np.uint8)
+    hs = np.zeros(I // 16, np.uint8)
+    _load().orc_moe4_glu_requant(g.ctypes.data, u.ctypes.data, I, float(Sh), hq.ctypes.data,
+                                 hs.ctypes.data)
+    return hq, hs
+
+
+def moe4_down(hq, hs, Sh, e, inp, H, I):
+    y = np.zeros(H)
+    by = np.zeros(H)
+    hq = np.ascontiguousarray(hq, dtype=np.uint8)
+    hs = np.ascontiguousarray(hs, dtype=np.uint8)
+    w2q, w2s = np.ascontiguousarray(inp["w2q"]), np.ascontiguousarray(inp["w2s"])
+    Sw2 = np.ascontiguousarray(inp["Sw2"], np.float32)
+    _load().orc_moe4_down(hq.ctypes.data, hs.ctypes.data, float(Sh), e, w2q.ctypes.data,
+                          w2s.ctypes.data, Sw2.ctypes.data, H, I, y.ctypes.data, by.ctypes.data)
+    return y, by
+
+
+def moe4_tokens(inp: dict, T, H, I, E, topk, tokens, nthreads=None):
+    """End-to-end NVFP4 MoE output (FP64) and bound for the listed tokens."""
+    tokens = np.ascontiguousarray(tokens, dtype=np.int64)
+    out = np.zeros((tokens.size, H))
+    bound = np.zeros((tokens.size, H))
+    a = {k: np.ascontiguousarray(v) for k, v in inp.items() if isinstance(v, np.ndarray)}
+    Sw13 = np.ascontiguousarray(inp["Sw13"], np.float32)
+    Sw2 = np.ascontiguousarray(inp["Sw2"], np.float32)
+    rc = _load().orc_moe4_tokens(a["xq"].ctypes.data, a["xs"].ctypes.data, float(inp["Sx"]),
+                                 a["ids"].ctypes.data, a["tw"].ctypes.data, T, H, I, E, topk,
+                                 a["w13q"].ctypes.data, a["w13s"].ctypes.data, Sw13.ctypes.data,
+                                 a["w2q"].ctypes.data, a["w2s"].ctypes.data, Sw2.ctypes.data,
+                                 float(inp["Sh"]), tokens.ctypes.data, tokens.size,
+                                 out.ctypes.data, bound.ctypes.data, _nthreads(nthreads))
+    if rc != 0:
+        raise ValueError("oracle: bad moe4 arguments")
     return out, bound

@@ -14,7 +14,9 @@
  *    scale) and the per-K=16 FP32 block-scale application on the FP8 MMA.
  *  - FlashInfer "swapab_cutedsl_megakernel" skill page, Layout section: the
  *    MXFP8 GLU mixture-of-experts (gate/up, GLU, down) whose generic reference
- *    the MoE functions below restate.
+ *    the MoE functions below restate, and the NVFP4 MoE the page lists beside
+ *    it (moe_nvfp4_swapab), whose computation is read here as the same GLU
+ *    MoE with every operand in NVFP4 (the orc_moe4_* functions).
  * Format definitions (E2M1, E4M3-FN, E8M0, BF16) are the OCP / IEEE ones; the
  * pages name the formats without defining their bits.
  */
@@ -427,5 +429,178 @@ int orc_moe_tokens(const uint8_t *xq, const uint8_t *xs, const int32_t *ids,
   orc_moe_ctx c = {xq, xs, ids, tw, T, H, I, E, topk,
                    w13q, w13s, w2q, w2s, tokens, out, bound};
   orc_parallel(ntok, nthreads, &c, orc_moe_range);
+  return 0;
+}
+
+/* ------------------------------------------------------------- NVFP4 MoE */
+/* The GLU MoE of the functions above with NVFP4 operands: x with one FP32
+ * tensor scale Sx, each expert's w13 and w2 with one FP32 tensor scale per
+ * expert, and h re-quantised to NVFP4 under a tensor scale Sh that the caller
+ * fixes.  Values decode exactly to FP64 and every sum runs in ascending k. */
+
+static double orc_nv_elem(const uint8_t *q, const uint8_t *s, int64_t row, int64_t K,
+                          int64_t k) {
+  uint8_t byte = q[row * (K / 2) + k / 2];
+  uint8_t code = (k & 1) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 15);
+  return orc_dec_e2m1(code) * orc_dec_e4m3(s[row * (K / 16) + k / 16]);
+}
+
+/* FP32 value -> E2M1 code (sign in bit 3): the nearest of the eight
+ * magnitudes, a tie going to the code with a zero low bit; magnitudes above 6
+ * give 6; NaN gives 0. */
+uint8_t orc_enc_e2m1_rne_sat(float v) {
+  if (isnan(v)) return 0;
+  uint8_t sgn = signbit(v) ? 8 : 0;
+  double a = fabs((double)v);
+  if (a >= 6.0) return sgn | 7; /* saturate (distances to 4 and 6 tie for huge a) */
+  int best = 0;
+  double bd = INFINITY;
+  for (int c = 0; c < 8; c++) {
+    double d = fabs(a - orc_dec_e2m1((uint8_t)c));
+    if (d < bd || (d == bd && (c & 1) == 0)) {
+      bd = d;
+      best = c;
+    }
+  }
+  return sgn | (uint8_t)best;
+}
+
+/* NVFP4 quantisation of n FP32 values (n % 16 == 0) under tensor scale S,
+ * taken in FP32: per group of 16, scale byte = E4M3(amax / 6 / S) (nearest
+ * even, saturating), then code = E2M1(v / (e4m3(scale) * S)); a zero scale
+ * gives zero codes.  Codes are packed two per byte, element 2j in the low
+ * nibble. */
+void orc_nvq(const float *v, int64_t n, float S, uint8_t *codes, uint8_t *scales) {
+  for (int64_t g = 0; g < n / 16; g++) {
+    float amax = 0.0f;
+    for (int64_t i = 0; i < 16; i++) {
+      float a = fabsf(v[16 * g + i]);
+      if (a > amax) amax = a;
+    }
+    float sv = amax / 6.0f / S;
+    uint8_t sb = orc_enc_e4m3_rne_sat((double)sv);
+    scales[g] = sb;
+    float d = (float)orc_dec_e4m3(sb) * S;
+    for (int64_t i = 0; i < 16; i += 2) {
+      uint8_t c0 = 0, c1 = 0;
+      if ((sb & 0x7F) != 0) {
+        c0 = orc_enc_e2m1_rne_sat(v[16 * g + i] / d);
+        c1 = orc_enc_e2m1_rne_sat(v[16 * g + i + 1] / d);
+      }
+      codes[(16 * g + i) / 2] = (uint8_t)(c0 | (c1 << 4));
+    }
+  }
+}
+
+void orc_moe4_gateup(const uint8_t *xq, const uint8_t *xs, float Sx, int64_t t, int64_t e,
+                     const uint8_t *w13q, const uint8_t *w13s, const float *Sw13, int64_t H,
+                     int64_t I, double *g, double *u, double *bg, double *bu) {
+  const double f = (double)Sx * (double)Sw13[e];
+  for (int64_t i = 0; i < I; i++) {
+    int64_t rg = e * 2 * I + i, ru = e * 2 * I + I + i;
+    double sg = 0, su = 0, ag = 0, au = 0;
+    for (int64_t k = 0; k < H; k++) {
+      double x = orc_nv_elem(xq, xs, t, H, k);
+      double pg = x * orc_nv_elem(w13q, w13s, rg, H, k);
+      double pu = x * orc_nv_elem(w13q, w13s, ru, H, k);
+      sg += pg;
+      su += pu;
+      ag += fabs(pg);
+      au += fabs(pu);
+    }
+    g[i] = f * sg;
+    u[i] = f * su;
+    if (bg) bg[i] = fabs(f) * ag;
+    if (bu) bu[i] = fabs(f) * au;
+  }
+}
+
+void orc_moe4_glu_requant(const double *g, const double *u, int64_t I, float Sh, uint8_t *hq,
+                          uint8_t *hs) {
+  float *h = (float *)malloc(sizeof(float) * (size_t)I);
+  for (int64_t i = 0; i < I; i++) {
+    double silu = g[i] / (1.0 + exp(-g[i]));
+    h[i] = (float)(silu * u[i]); /* the requant decisions are taken in FP32 */
+  }
+  orc_nvq(h, I, Sh, hq, hs);
+  free(h);
+}
+
+void orc_moe4_down(const uint8_t *hq, const uint8_t *hs, float Sh, int64_t e,
+                   const uint8_t *w2q, const uint8_t *w2s, const float *Sw2, int64_t H,
+                   int64_t I, double *y, double *by) {
+  const double f = (double)Sh * (double)Sw2[e];
+  for (int64_t n = 0; n < H; n++) {
+    double s = 0, a = 0;
+    for (int64_t i = 0; i < I; i++) {
+      double p = orc_nv_elem(hq, hs, 0, I, i) * orc_nv_elem(w2q, w2s, e * H + n, I, i);
+      s += p;
+      a += fabs(p);
+    }
+    y[n] = f * s;
+    if (by) by[n] = fabs(f) * a;
+  }
+}
+
+typedef struct {
+  const uint8_t *xq, *xs;
+  float Sx, Sh;
+  const int32_t *ids;
+  const float *tw;
+  int64_t T, H, I, E, topk;
+  const uint8_t *w13q, *w13s, *w2q, *w2s;
+  const float *Sw13, *Sw2;
+  const int64_t *tokens;
+  double *out, *bound;
+} orc_moe4_ctx;
+
+static void orc_moe4_range(void *p, int64_t lo, int64_t hi) {
+  orc_moe4_ctx *c = (orc_moe4_ctx *)p;
+  const int64_t H = c->H, I = c->I;
+  double *g = (double *)malloc(sizeof(double) * (size_t)I);
+  double *u = (double *)malloc(sizeof(double) * (size_t)I);
+  double *y = (double *)malloc(sizeof(double) * (size_t)H);
+  double *by = (double *)malloc(sizeof(double) * (size_t)H);
+  uint8_t *hq = (uint8_t *)malloc((size_t)(I / 2));
+  uint8_t *hs = (uint8_t *)malloc((size_t)(I / 16));
+  for (int64_t ti = lo; ti < hi; ti++) {
+    int64_t t = c->tokens[ti];
+    double *o = c->out + ti * H, *b = c->bound + ti * H;
+    for (int64_t n = 0; n < H; n++) o[n] = b[n] = 0.0;
+    for (int64_t j = 0; j < c->topk; j++) {
+      int64_t e = c->ids[t * c->topk + j];
+      double w = (double)c->tw[t * c->topk + j];
+      orc_moe4_gateup(c->xq, c->xs, c->Sx, t, e, c->w13q, c->w13s, c->Sw13, H, I, g, u, NULL,
+                      NULL);
+      orc_moe4_glu_requant(g, u, I, c->Sh, hq, hs);
+      orc_moe4_down(hq, hs, c->Sh, e, c->w2q, c->w2s, c->Sw2, H, I, y, by);
+      for (int64_t n = 0; n < H; n++) {
+        o[n] += w * y[n];
+        b[n] += fabs(w) * by[n];
+      }
+    }
+  }
+  free(g); free(u); free(y); free(by); free(hq); free(hs);
+}
+
+int orc_moe4_tokens(const uint8_t *xq, const uint8_t *xs, float Sx, const int32_t *ids,
+                    const float *tw, int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk,
+                    const uint8_t *w13q, const uint8_t *w13s, const float *Sw13,
+                    const uint8_t *w2q, const uint8_t *w2s, const float *Sw2, float Sh,
+                    const int64_t *tokens, int64_t ntok, double *out, double *bound,
+                    int nthreads) {
+  if (!xq || !xs || !ids || !tw || !w13q || !w13s || !Sw13 || !w2q || !w2s || !Sw2) return -1;
+  if (H % 16 || I % 16 || H <= 0 || I <= 0 || E <= 0 || topk <= 0) return -1;
+  if (ntok < 0 || (ntok > 0 && (!tokens || !out || !bound))) return -1;
+  for (int64_t i = 0; i < ntok; i++) {
+    if (tokens[i] < 0 || tokens[i] >= T) return -1;
+    for (int64_t j = 0; j < topk; j++) {
+      int32_t e = ids[tokens[i] * topk + j];
+      if (e < 0 || e >= E) return -1;
+    }
+  }
+  orc_moe4_ctx c = {xq, xs, Sx, Sh, ids, tw, T, H, I, E, topk,
+                    w13q, w13s, w2q, w2s, Sw13, Sw2, tokens, out, bound};
+  orc_parallel(ntok, nthreads, &c, orc_moe4_range);
   return 0;
 }

@@ -121,6 +121,37 @@ int orc_moe_tokens(const uint8_t *xq, const uint8_t *xs, const int32_t *ids,
 /* round-to-nearest-even of an FP64 value to BF16 bits (no double rounding) */
 uint16_t orc_bf16_rne(double v);
 
+/* --- NVFP4 grouped MoE GLU: the MoE above with NVFP4 operands ---
+   x: codes [T,H/2] (element 2j in the low nibble), E4M3 scales [T,H/16],
+   FP32 tensor scale Sx.  w13 [E,2I,H/2] + [E,2I,H/16], one FP32 tensor scale
+   per expert Sw13[E]; w2 [E,H,I/2] + [E,H,I/16], Sw2[E].  h is re-quantised
+   to NVFP4 under the caller's tensor scale Sh. */
+/* FP32 -> E2M1 code: nearest magnitude of {0,.5,1,1.5,2,3,4,6}, ties to the
+   code with a zero low bit, saturating at 6, sign in bit 3; NaN -> 0 */
+uint8_t orc_enc_e2m1_rne_sat(float v);
+/* NVFP4 quantiser taken in FP32: per 16, scale = E4M3(amax / 6 / S), codes =
+   E2M1(v / (e4m3(scale) * S)); a zero scale gives zero codes.  n % 16 == 0;
+   codes packed two per byte. */
+void orc_nvq(const float *v, int64_t n, float S, uint8_t *codes, uint8_t *scales);
+/* g = Sx Sw13[e] sum_k x_k w13[e][i]_k, u likewise for row I+i, and bounds */
+void orc_moe4_gateup(const uint8_t *xq, const uint8_t *xs, float Sx, int64_t t, int64_t e,
+                     const uint8_t *w13q, const uint8_t *w13s, const float *Sw13, int64_t H,
+                     int64_t I, double *g, double *u, double *bg, double *bu);
+/* h = silu(g) * u in FP64, rounded to FP32, then orc_nvq under Sh */
+void orc_moe4_glu_requant(const double *g, const double *u, int64_t I, float Sh, uint8_t *hq,
+                          uint8_t *hs);
+/* y[n] = Sh Sw2[e] sum_i dec(hq)_i dec(w2[e][n])_i, and its bound */
+void orc_moe4_down(const uint8_t *hq, const uint8_t *hs, float Sh, int64_t e,
+                   const uint8_t *w2q, const uint8_t *w2s, const float *Sw2, int64_t H,
+                   int64_t I, double *y, double *by);
+/* end to end for the listed tokens, as orc_moe_tokens */
+int orc_moe4_tokens(const uint8_t *xq, const uint8_t *xs, float Sx, const int32_t *ids,
+                    const float *tw, int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk,
+                    const uint8_t *w13q, const uint8_t *w13s, const float *Sw13,
+                    const uint8_t *w2q, const uint8_t *w2s, const float *Sw2, float Sh,
+                    const int64_t *tokens, int64_t ntok, double *out, double *bound,
+                    int nthreads);
+
 #ifdef __cplusplus
 }
 #endif

@@ -314,3 +314,35 @@ def moe(T, H, I, E, topk, seed=0, w_std=0.02):
     del w2
     ids, tw = topk_routing(T, E, topk, seed)
     return dict(xq=xq, xs=xs, w13q=w13q, w13s=w13s, w2q=w2q, w2s=w2s, ids=ids, tw=tw)
+
+
+# static tensor scale of the NVFP4 re-quantisation of h in the NVFP4 MoE
+# (the caller fixes it; 2^-8 puts the group scales amax / 6 / S_h of the
+# workload's h, |h| within about 2^-7 .. 2^4, inside the E4M3 range)
+MOE4_SH = 2.0 ** -8
+
+
+def moe_nvfp4(T, H, I, E, topk, seed=0, w_std=0.02):
+    """NVFP4 MoE inputs: x ~ N(0,1) and the experts' w13, w2 ~ N(0, w_std)
+    quantised to NVFP4 (x with one tensor scale, each expert's matrices with
+    their own), the same routing as moe()."""
+    x = normal((T, H), 1.0, seed, ROLE_A)
+    xq, xs, Sx = quant_nvfp4(x)
+    del x
+    w13q = np.empty((E, 2 * I, H // 2), np.uint8)
+    w13s = np.empty((E, 2 * I, H // 16), np.uint8)
+    w2q = np.empty((E, H, I // 2), np.uint8)
+    w2s = np.empty((E, H, I // 16), np.uint8)
+    Sw13 = np.empty(E, np.float32)
+    Sw2 = np.empty(E, np.float32)
+    w13 = normal((E, 2 * I, H), w_std, seed, ROLE_W)
+    for e in range(E):
+        w13q[e], w13s[e], Sw13[e] = quant_nvfp4(w13[e])
+    del w13
+    w2 = normal((E, H, I), w_std, seed, ROLE_W2)
+    for e in range(E):
+        w2q[e], w2s[e], Sw2[e] = quant_nvfp4(w2[e])
+    del w2
+    ids, tw = topk_routing(T, E, topk, seed)
+    return dict(xq=xq, xs=xs, Sx=Sx, w13q=w13q, w13s=w13s, Sw13=Sw13, w2q=w2q, w2s=w2s, Sw2=Sw2,
+                Sh=np.float32(MOE4_SH), ids=ids, tw=tw)
