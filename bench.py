@@ -43,7 +43,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quick", action="store_true", help="headline kernel only")
-    ap.add_argument("--only", default="", help="w4a4|w4a8|bf16|moe|moe_decode (profiling runs)")
+    ap.add_argument("--only", default="",
+                    help="w4a4|w4a8|bf16|moe|moe_decode|moe_nvfp4 (profiling runs)")
     ap.add_argument("--moe-dec-tokens", default="1,16",
                     help="token counts of the decode-sized MoE calls")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -283,6 +284,28 @@ def main():
         del dm, o
         torch.cuda.empty_cache()
 
+    # ---------------------------------------------------- NVFP4 MoE (W4A4 route)
+    if args.only in ("", "moe_nvfp4") and not args.quick:
+        T, H, I, E, topk = 4096, 4096, 1536, 64, 8
+        m4 = synth.moe_nvfp4(T, H, I, E, topk, seed=0)
+        d4 = {k: todev(v) for k, v in m4.items() if k not in ("Sx", "Sh")}
+        o4 = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        ws4 = mg.workspace(mg.mgemm_workspace_bytes(mg.OP_MOE_NVFP4, T=T, H=H, I=I, E=E, topk=topk),
+                           "moe_nvfp4")
+        sx, sh = f32(m4["Sx"]), f32(m4["Sh"])
+        call4 = lambda i: mg.mgemm_moe_nvfp4_glu(  # noqa: E731
+            d4["xq"], d4["xs"], sx, d4["ids"], d4["tw"], d4["w13q"], d4["w13s"], d4["Sw13"],
+            d4["w2q"], d4["w2s"], d4["Sw2"], sh, o4, ws=ws4)
+        ms = timed(torch, call4, max(3, args.steps // 2), min(args.warmup, 10), stream)
+        fl = 2.0 * T * topk * (H * 2 * I + I * H)
+        tf = fl / (ms * 1e-3) / 1e12
+        fmas = T * topk * (H * 2 * I + I * H) / 16          # per-group scale FMAs
+        out["moe_nvfp4"] = {"T": T, "H": H, "I": I, "E": E, "topk": topk, "ms": round(ms, 3),
+                            "tflops": round(tf, 1), "frac_fp8_peak": round(tf / PEAK["fp8"], 4),
+                            "route_fma_tflops": round(2 * fmas / (ms * 1e-3) / 1e12, 2)}
+        del d4, o4, m4
+        torch.cuda.empty_cache()
+
     if args.copy_calib_mib:
         n = args.copy_calib_mib * (1 << 20) // 4
         x = torch.ones(n, dtype=torch.float32, device=dev)
@@ -346,6 +369,7 @@ def main():
         "bf16": out.get("bf16"),
         "moe": out.get("moe"),
         "moe_decode": out.get("moe_decode"),
+        "moe_nvfp4": out.get("moe_nvfp4"),
         "device": torch.cuda.get_device_properties(0).gcnArchName,
         "kernel_src": src_hash("gemm_w4a4.hip", "common.h"),
     }

@@ -31,7 +31,7 @@ LIB_PATH = os.path.join(_HERE, "libmgemm.so")
 FMT_BF16, FMT_NVFP4, FMT_FP8_E4M3_TOKEN, FMT_MXFP8 = 0, 1, 2, 3
 EXEC_NATIVE, EXEC_FP8_EXACT, EXEC_NOPATH = 0, 1, 2
 MMA_NONE, MMA_BF16, MMA_FP8, MMA_MX_F8F6F4 = 0, 1, 2, 3
-OP_BF16, OP_W4A16, OP_W4A8, OP_W4A4, OP_MOE = 0, 1, 2, 3, 4
+OP_BF16, OP_W4A16, OP_W4A8, OP_W4A4, OP_MOE, OP_MOE_NVFP4 = 0, 1, 2, 3, 4, 5
 
 EXEC_NAMES = {EXEC_NATIVE: "native", EXEC_FP8_EXACT: "fp8_exact", EXEC_NOPATH: "nopath"}
 MMA_NAMES = {MMA_NONE: "none", MMA_BF16: "bf16", MMA_FP8: "fp8", MMA_MX_F8F6F4: "mx_f8f6f4"}
@@ -72,6 +72,8 @@ def load() -> C.CDLL:
         "mgemm_w4a4": (i32, [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]),
         "mgemm_moe_mxfp8_glu": (i32, [vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, vp, vp, vp,
                                       vp, vp, C.c_size_t, vp, vp]),
+        "mgemm_moe_nvfp4_glu": (i32, [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, vp, vp,
+                                      vp, vp, vp, vp, vp, vp, C.c_size_t, vp, vp]),
         "mgemm_workspace_bytes": (C.c_size_t, [i32, i64, i64, i64, i64, i64, i64, i64, i64]),
         "mgemm_status_string": (C.c_char_p, [i32]),
         "mgemm_version": (C.c_char_p, []),
@@ -270,4 +272,42 @@ def mgemm_moe_mxfp8_glu(xq, xs, topk_ids, topk_w, w13q, w13s, w2q, w2s, out,
         w13q.data_ptr(), w13s.data_ptr(), w2q.data_ptr(), w2s.data_ptr(), out.data_ptr(),
         ws.data_ptr(), ws.numel() * ws.element_size(),
         dbg_h.data_ptr() if dbg_h is not None else None, _stream(stream)))
+    return out
+
+
+def mgemm_moe_nvfp4_glu(xq, xs, Sx, topk_ids, topk_w, w13q, w13s, Sw13, w2q, w2s, Sw2, Sh, out,
+                        ws: Optional[torch.Tensor] = None, dbg_h: Optional[torch.Tensor] = None,
+                        stream=None):
+    """NVFP4 grouped MoE GLU; Sx, Sh: FP32 [1], Sw13, Sw2: FP32 [E] (device)."""
+    T, H2 = xq.shape
+    H = 2 * H2
+    topk = topk_ids.shape[1]
+    E, I2, _ = w13q.shape
+    I = I2 // 2
+    _need(xq, "xq", _U8, (T, H // 2))
+    _need(xs, "xs", _U8, (T, H // 16))
+    _need(Sx, "Sx", _F32, numel=1)
+    _need(topk_ids, "topk_ids", (torch.int32,), (T, topk))
+    _need(topk_w, "topk_w", _F32, (T, topk))
+    _need(w13q, "w13q", _U8, (E, 2 * I, H // 2))
+    _need(w13s, "w13s", _U8, (E, 2 * I, H // 16))
+    _need(Sw13, "Sw13", _F32, numel=E)
+    _need(w2q, "w2q", _U8, (E, H, I // 2))
+    _need(w2s, "w2s", _U8, (E, H, I // 16))
+    _need(Sw2, "Sw2", _F32, numel=E)
+    _need(Sh, "Sh", _F32, numel=1)
+    _need(out, "out", (torch.bfloat16,), (T, H))
+    if dbg_h is not None:
+        _need(dbg_h, "dbg_h", _U8, numel=T * topk * (I // 2 + I // 16))
+    need = mgemm_workspace_bytes(OP_MOE_NVFP4, T=T, H=H, I=I, E=E, topk=topk)
+    if ws is None:
+        ws = workspace(need, "moe_nvfp4")
+    if ws.numel() * ws.element_size() < need:
+        raise ValueError("moe_nvfp4: workspace too small")
+    _check("mgemm_moe_nvfp4_glu", load().mgemm_moe_nvfp4_glu(
+        xq.data_ptr(), xs.data_ptr(), Sx.data_ptr(), topk_ids.data_ptr(), topk_w.data_ptr(),
+        T, H, I, E, topk, w13q.data_ptr(), w13s.data_ptr(), Sw13.data_ptr(), w2q.data_ptr(),
+        w2s.data_ptr(), Sw2.data_ptr(), Sh.data_ptr(), out.data_ptr(), ws.data_ptr(),
+        ws.numel() * ws.element_size(), dbg_h.data_ptr() if dbg_h is not None else None,
+        _stream(stream)))
     return out

@@ -229,6 +229,34 @@ int mgemm_moe_mxfp8_glu(const void *xq, const void *xs, const int32_t *topk_ids,
   return finish(mg::launch_moe(p, (hipStream_t)stream), "mgemm_moe_mxfp8_glu");
 }
 
+int mgemm_moe_nvfp4_glu(const void *xq, const void *xs, const float *Sx,
+                        const int32_t *topk_ids, const float *topk_w, int64_t T, int64_t H,
+                        int64_t I, int64_t E, int64_t topk, const void *w13q,
+                        const void *w13s, const float *Sw13, const void *w2q,
+                        const void *w2s, const float *Sw2, const float *Sh, void *out,
+                        void *ws, size_t ws_bytes, void *dbg_h, void *stream) {
+  if (!xq || !xs || !Sx || !topk_ids || !topk_w || !w13q || !w13s || !Sw13 || !w2q || !w2s ||
+      !Sw2 || !Sh || !out)
+    return MGEMM_ERR_INVALID_ARG;
+  if (!aligned16(xq) || !aligned16(xs) || !aligned16(topk_ids) || !aligned16(topk_w) ||
+      !aligned16(w13q) || !aligned16(w13s) || !aligned16(w2q) || !aligned16(w2s) ||
+      !aligned16(out) || ((uintptr_t)Sx & 3) || ((uintptr_t)Sw13 & 3) || ((uintptr_t)Sw2 & 3) ||
+      ((uintptr_t)Sh & 3))
+    return MGEMM_ERR_INVALID_ARG;
+  if (T <= 0 || H <= 0 || I <= 0 || E <= 0 || topk <= 0) return MGEMM_ERR_SHAPE;
+  if (H % 32 != 0 || I % 64 != 0 || topk > 16 || E > 1024 || T > (1 << 24) ||
+      H > (1 << 20) || I > (1 << 20) || (double)T * topk * (double)(H > I ? H : I) > 4.0e18)
+    return MGEMM_ERR_SHAPE;
+  if (int rc = check_path(MGEMM_FMT_NVFP4, MGEMM_FMT_NVFP4)) return rc;
+  const size_t need = mg::moe4_workspace_bytes(T, H, I, E, topk);
+  if (!ws || ws_bytes < need || !aligned16(ws)) return MGEMM_ERR_WORKSPACE;
+  mg::Moe4Args p{(const uint8_t *)xq, (const uint8_t *)xs, Sx, topk_ids, topk_w, (int)T, (int)H,
+                 (int)I, (int)E, (int)topk, (const uint8_t *)w13q, (const uint8_t *)w13s, Sw13,
+                 (const uint8_t *)w2q, (const uint8_t *)w2s, Sw2, Sh, (uint16_t *)out, ws,
+                 ws_bytes, (uint8_t *)dbg_h};
+  return finish(mg::launch_moe4(p, (hipStream_t)stream), "mgemm_moe_nvfp4_glu");
+}
+
 size_t mgemm_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int64_t T, int64_t H,
                              int64_t I, int64_t E, int64_t topk) {
   switch (op) {
@@ -244,6 +272,11 @@ size_t mgemm_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int64_t T,
           H % 64 != 0 || I % 64 != 0)
         return 0;
       return mg::moe_workspace_bytes(T, H, I, E, topk);
+    case MGEMM_OP_MOE_NVFP4:
+      if (T <= 0 || H <= 0 || I <= 0 || E <= 0 || topk <= 0 || topk > 16 || E > 1024 ||
+          H % 32 != 0 || I % 64 != 0)
+        return 0;
+      return mg::moe4_workspace_bytes(T, H, I, E, topk);
   }
   return 0;
 }

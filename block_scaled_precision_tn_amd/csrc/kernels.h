@@ -62,4 +62,31 @@ struct MoeArgs {
 size_t moe_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk);
 hipError_t launch_moe(const MoeArgs &p, hipStream_t stream);
 
+// NVFP4 grouped MoE GLU (x, w13, w2 and h in NVFP4; tensor scales are device
+// FP32: Sx, Sh one value, Sw13 / Sw2 one per expert)
+struct Moe4Args {
+  const uint8_t *xq, *xs;
+  const float *Sx;
+  const int32_t *ids;
+  const float *tw;
+  int T, H, I, E, topk;
+  const uint8_t *w13q, *w13s;
+  const float *Sw13;
+  const uint8_t *w2q, *w2s;
+  const float *Sw2;
+  const float *Sh;
+  uint16_t *out;
+  void *ws;
+  size_t ws_bytes;
+  uint8_t *dbg_h;   // optional: per entry, I/2 code bytes then I/16 scale bytes
+};
+size_t moe4_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk);
+hipError_t launch_moe4(const Moe4Args &p, hipStream_t stream);
+// the grouped W4A4 GEMMs of the NVFP4 MoE (moe4.hip), on the routing that
+// launch_moe4 (moe.hip) has written to the workspace
+hipError_t launch_moe4_gemms(const Moe4Args &p, const int32_t *meta, const int32_t *sorted,
+                             const float *wsorted, const int32_t *tile_e, const int32_t *tile_r,
+                             const int32_t *tile_n, int maxtiles, uint8_t *hq, uint8_t *hs,
+                             float *y, hipStream_t stream);
+
 }  // namespace mg

@@ -25,6 +25,7 @@
 //            rows of (t, j), then BF16 (deterministic: no atomics)
 #include "common.h"
 #include "kernels.h"
+#include "quant.h"
 
 namespace mg {
 namespace {
@@ -41,7 +42,9 @@ struct Layout {
 
 size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-Layout layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk) {
+// fp4: h stored as NVFP4 (I/2 code bytes, I/16 scale bytes per row) rather
+// than MXFP8 (I, I/32)
+Layout layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk, bool fp4 = false) {
   Layout L;
   L.R = (int)(T * topk);
   L.maxtiles = (int)((L.R + BM - 1) / BM + E);
@@ -55,8 +58,8 @@ Layout layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk) {
   L.tile_e = o; o += up256(sizeof(int32_t) * (size_t)L.maxtiles);
   L.tile_r = o; o += up256(sizeof(int32_t) * (size_t)L.maxtiles);
   L.tile_n = o; o += up256(sizeof(int32_t) * (size_t)L.maxtiles);
-  L.hq = o;     o += up256((size_t)L.R * (size_t)I);
-  L.hs = o;     o += up256((size_t)L.R * (size_t)(I / 32));
+  L.hq = o;     o += up256((size_t)L.R * (size_t)(fp4 ? I / 2 : I));
+  L.hs = o;     o += up256((size_t)L.R * (size_t)(fp4 ? I / 16 : I / 32));
   L.y = o;      o += up256(sizeof(float) * (size_t)L.R * (size_t)H);  // weighted down rows
   L.total = o;
   return L;
@@ -348,22 +351,6 @@ __device__ __forceinline__ void mx_mainloop(const MxRows &rows, int Ktot, const 
     mx_mainloop_sc16<NB>(rows, Ktot, bsel, acc);
   else
     mx_mainloop_sc2<NB>(rows, Ktot, bsel, acc);
-}
-
-// FP32 -> E4M3-FN byte, nearest even, saturating at +-448 (NaN -> 0x7F)
-__device__ __forceinline__ uint32_t f32_to_e4m3_rne_sat(float v) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, v);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t au = u & 0x7FFFFFFFu;
-  if (au > 0x7F800000u) return 0x7Fu;
-  const float a = __builtin_bit_cast(float, au);
-  if (!(a < 448.0f)) return sign | 0x7Eu;
-  if (a < 0.015625f) {                   // below 2^-6: steps of 2^-9
-    const uint32_t m = (uint32_t)__builtin_rintf(a * 512.0f);
-    return sign | m;                      // m == 8 is the smallest normal, code 0x08
-  }
-  const uint32_t r = (au + 0x7FFFFu + ((au >> 20) & 1u)) >> 20;  // 8-bit exp | 3-bit mantissa
-  return sign | (r - (120u << 3));
 }
 
 __device__ __forceinline__ float max32_lanes(float v) {
@@ -861,6 +848,55 @@ hipError_t launch_moe(const MoeArgs &p, hipStream_t stream) {
                        tile_n, hq, hs, y);
   hipLaunchKernelGGL(k_combine, dim3((unsigned)((TH4 + 255) / 256)), dim3(256), 0, stream, y, pos,
                      p.T, p.H, p.topk, p.out);
+  return hipGetLastError();
+}
+
+}  // namespace mg
+
+namespace mg {
+
+size_t moe4_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk) {
+  return layout(T, H, I, E, topk, true).total;
+}
+
+// NVFP4 MoE: the routing and the combine of the MXFP8 MoE around the grouped
+// W4A4 GEMMs of moe4.hip
+hipError_t launch_moe4(const Moe4Args &p, hipStream_t stream) {
+  const Layout L = layout(p.T, p.H, p.I, p.E, p.topk, true);
+  char *w = (char *)p.ws;
+  uint32_t *counts = (uint32_t *)(w + L.counts);
+  int32_t *offs = (int32_t *)(w + L.offs);
+  int32_t *meta = (int32_t *)(w + L.meta);
+  int32_t *sorted = (int32_t *)(w + L.sorted);
+  int32_t *pos = (int32_t *)(w + L.pos);
+  float *wsorted = (float *)(w + L.wsorted);
+  int32_t *tile_e = (int32_t *)(w + L.tile_e);
+  int32_t *tile_r = (int32_t *)(w + L.tile_r);
+  int32_t *tile_n = (int32_t *)(w + L.tile_n);
+  uint8_t *hq = (uint8_t *)(w + L.hq);
+  uint8_t *hs = (uint8_t *)(w + L.hs);
+  float *y = (float *)(w + L.y);
+  const int64_t TH4 = (int64_t)p.T * (p.H / 4);
+  if (L.R <= 1024) {
+    hipLaunchKernelGGL(k_route_small, dim3(1), dim3(1024), 0, stream, p.ids, p.tw, L.R, p.E, offs,
+                       meta, tile_e, tile_r, tile_n, pos, sorted, wsorted);
+  } else {
+    const int rb = (L.R + 255) / 256;
+    hipLaunchKernelGGL(k_prep, dim3((p.E + 255) / 256), dim3(256), 0, stream, counts, p.E);
+    hipLaunchKernelGGL(k_count, dim3((L.R + 1023) / 1024), dim3(1024), 0, stream, p.ids, L.R,
+                       p.E, counts, pos);
+    hipLaunchKernelGGL(k_scan, dim3(1), dim3(256), 0, stream, counts, p.E, offs, meta, tile_e,
+                       tile_r, tile_n);
+    hipLaunchKernelGGL(k_scatter, dim3(rb), dim3(256), 0, stream, p.ids, p.tw, L.R, offs, pos,
+                       sorted, wsorted);
+  }
+  // every active tile has at least one row: at most R tiles
+  const int ty = L.maxtiles < L.R ? L.maxtiles : L.R;
+  hipError_t e = launch_moe4_gemms(p, meta, sorted, wsorted, tile_e, tile_r, tile_n, ty, hq, hs,
+                                   y, stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_combine, dim3((unsigned)((TH4 + 255) / 256)), dim3(256), 0, stream, y,
+                     pos, p.T, p.H, p.topk, p.out);
   return hipGetLastError();
 }
 

@@ -191,9 +191,37 @@ int mgemm_moe_mxfp8_glu(const void *xq, const void *xs, const int32_t *topk_ids,
                         const void *w2q, const void *w2s, void *out, void *ws,
                         size_t ws_bytes, void *dbg_h, void *stream);
 
+/* NVFP4 grouped mixture-of-experts GLU: the GLU MoE above (same FlashInfer
+   skill page, which lists an NVFP4 MoE, moe_nvfp4_swapab, beside the MXFP8
+   one) with every operand in NVFP4, computed on the exact FP8 route of the
+   metrale_circuit hardware::exec module description (as mgemm_w4a4: NVFP4
+   activations have no block-scaled MMA on gfx950).  Inputs: xq [T,H/2] E2M1
+   codes (element 2j in the low nibble) and xs [T,H/16] E4M3 scales, Sx one
+   FP32 tensor scale; w13q [E,2I,H/2] with w13s [E,2I,H/16] and Sw13 [E] (one
+   FP32 tensor scale per expert; rows [0,I) gate, [I,2I) up); w2q [E,H,I/2]
+   with w2s [E,H,I/16] and Sw2 [E]; Sh: the FP32 tensor scale under which h is
+   re-quantised; topk_ids, topk_w as for the MXFP8 MoE.  Per token t, slot j,
+   expert e: g, u = Sx Sw13[e] (x_t . w13[e]^T); h = silu(g) * u (FP32);
+   h -> NVFP4 per 16 along I, decided in FP32: scale = E4M3(amax / 6 / Sh)
+   (nearest even, saturating), code = E2M1(h / (scale * Sh)) (nearest, ties
+   to the even code, saturating at 6; a zero scale gives zero codes);
+   y = Sh Sw2[e] (h . w2[e]^T); out[t] = sum_j topk_w[t,j] y in FP32, BF16.
+   All FP32 scales are device pointers.  ws: at least
+   mgemm_workspace_bytes(MGEMM_OP_MOE_NVFP4, ...) bytes, no particular
+   contents needed.  dbg_h: NULL, or T*topk*(I/2 + I/16) bytes receiving each
+   (token, slot) row of the re-quantised h (I/2 code bytes, I/16 scale bytes)
+   at row t*topk + j.  H a multiple of 32, I a multiple of 64, topk in
+   [1,16], E in [1,1024], T <= 2^24.  Results are run-to-run bit-identical. */
+int mgemm_moe_nvfp4_glu(const void *xq, const void *xs, const float *Sx,
+                        const int32_t *topk_ids, const float *topk_w, int64_t T, int64_t H,
+                        int64_t I, int64_t E, int64_t topk, const void *w13q,
+                        const void *w13s, const float *Sw13, const void *w2q,
+                        const void *w2s, const float *Sw2, const float *Sh, void *out,
+                        void *ws, size_t ws_bytes, void *dbg_h, void *stream);
+
 /* workspace sizes */
 enum { MGEMM_OP_BF16 = 0, MGEMM_OP_W4A16 = 1, MGEMM_OP_W4A8 = 2, MGEMM_OP_W4A4 = 3,
-       MGEMM_OP_MOE = 4 };
+       MGEMM_OP_MOE = 4, MGEMM_OP_MOE_NVFP4 = 5 };
 /* Bytes of device workspace an op needs for these sizes (0 if none).  For the
    GEMMs pass (M, N, K) and zeros; for the MoE pass (T, H, I, E, topk) in the
    T.. arguments.  Returns 0 for unknown ops or invalid sizes as well. */
