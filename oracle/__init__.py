@@ -95,6 +95,8 @@ def _load():
     lib.orc_moe4_tokens.restype = C.c_int
     lib.orc_moe4_tokens.argtypes = [C.c_void_p, C.c_void_p, f32, C.c_void_p, C.c_void_p] + \
         [i64] * 5 + [C.c_void_p] * 6 + [f32, C.c_void_p, i64, C.c_void_p, C.c_void_p, C.c_int]
+    lib.orc_topk_softmax.restype = C.c_int
+    lib.orc_topk_softmax.argtypes = [C.c_void_p, i64, i64, i64, C.c_void_p, C.c_void_p]
     _lib = lib
     return lib
 
@@ -366,3 +368,15 @@ def moe4_tokens(inp: dict, T, H, I, E, topk, tokens, nthreads=None):
     if rc != 0:
         raise ValueError("oracle: bad moe4 arguments")
     return out, bound
+
+
+# ---------------------------------------------------------- top-k routing
+def topk_softmax(logits, topk):
+    """(ids int32 [T,topk], weights float32 [T,topk]) of FP32 logits [T,E]."""
+    lg = np.ascontiguousarray(logits, dtype=np.float32)
+    T, E = lg.shape
+    ids = np.zeros((T, topk), np.int32)
+    w = np.zeros((T, topk), np.float32)
+    if _load().orc_topk_softmax(lg.ctypes.data, T, E, topk, ids.ctypes.data, w.ctypes.data) != 0:
+        raise ValueError("oracle: bad routing arguments")
+    return ids, w

@@ -604,3 +604,39 @@ int orc_moe4_tokens(const uint8_t *xq, const uint8_t *xs, float Sx, const int32_
   orc_parallel(ntok, nthreads, &c, orc_moe4_range);
   return 0;
 }
+
+/* --------------------------------------------------------- top-k routing */
+/* Routing of the MoE configuration (softmax of the router logits, top k):
+ * per token, p_e = exp(l_e - max l) / sum_e' exp(l_e' - max l) in FP64; the k
+ * experts of largest p in descending order, equal p going to the lower id;
+ * weights the probabilities themselves (not renormalised), rounded to FP32.
+ * The order is taken on the logits, which gives the order of the exact
+ * probabilities (the softmax is increasing in the logit) without the ties an
+ * FP64 exp could create between distinct logits. */
+int orc_topk_softmax(const float *logits, int64_t T, int64_t E, int64_t topk, int32_t *ids,
+                     float *w) {
+  if (!logits || !ids || !w || T < 0 || E <= 0 || topk <= 0 || topk > E) return -1;
+  double *p = (double *)malloc(sizeof(double) * (size_t)E);
+  unsigned char *used = (unsigned char *)malloc((size_t)E);
+  for (int64_t t = 0; t < T; t++) {
+    const float *l = logits + t * E;
+    double m = -INFINITY, s = 0.0;
+    for (int64_t e = 0; e < E; e++) if ((double)l[e] > m) m = (double)l[e];
+    for (int64_t e = 0; e < E; e++) {
+      p[e] = exp((double)l[e] - m);
+      s += p[e];
+      used[e] = 0;
+    }
+    for (int64_t j = 0; j < topk; j++) {
+      int64_t best = -1;
+      for (int64_t e = 0; e < E; e++)
+        if (!used[e] && (best < 0 || l[e] > l[best])) best = e;
+      used[best] = 1;
+      ids[t * topk + j] = (int32_t)best;
+      w[t * topk + j] = (float)(p[best] / s);
+    }
+  }
+  free(p);
+  free(used);
+  return 0;
+}

@@ -152,6 +152,14 @@ int orc_moe4_tokens(const uint8_t *xq, const uint8_t *xs, float Sx, const int32_
                     const int64_t *tokens, int64_t ntok, double *out, double *bound,
                     int nthreads);
 
+/* --- top-k softmax routing of the MoE configuration ---
+   Per token t: p = softmax(logits[t,:]) in FP64; the topk experts of largest
+   p, descending, equal p to the lower id (ordered on the logits, which is the
+   order of the exact probabilities); w = p rounded to FP32 (not
+   renormalised).  logits [T,E] finite FP32; ids, w [T,topk]. */
+int orc_topk_softmax(const float *logits, int64_t T, int64_t E, int64_t topk, int32_t *ids,
+                     float *w);
+
 #ifdef __cplusplus
 }
 #endif

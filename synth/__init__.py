@@ -346,3 +346,8 @@ def moe_nvfp4(T, H, I, E, topk, seed=0, w_std=0.02):
     ids, tw = topk_routing(T, E, topk, seed)
     return dict(xq=xq, xs=xs, Sx=Sx, w13q=w13q, w13s=w13s, Sw13=Sw13, w2q=w2q, w2s=w2s, Sw2=Sw2,
                 Sh=np.float32(MOE4_SH), ids=ids, tw=tw)
+
+
+def moe_logits(T: int, E: int, seed: int = 0) -> np.ndarray:
+    """Router logits [T,E] ~N(0,1) in FP32 (the draw topk_routing uses)."""
+    return role_rng(seed, ROLE_LOGITS).standard_normal(size=(T, E)).astype(np.float32)
