@@ -262,6 +262,17 @@ def main():
             tf = fl / (ms * 1e-3) / 1e12
             out["moe"] = {"T": T, "H": H, "I": I, "E": E, "topk": topk, "ms": round(ms, 3),
                           "tflops": round(tf, 1), "frac_fp8_peak": round(tf / PEAK["fp8"], 4)}
+        # the router top-k that produces such ids and weights (FP32 logits)
+        if args.only != "moe_decode":
+            lg = todev(synth.moe_logits(T, E, seed=0))
+            rids = torch.empty((T, topk), dtype=torch.int32, device=dev)
+            rw = torch.empty((T, topk), dtype=torch.float32, device=dev)
+            callr = lambda i: mg.mgemm_moe_route_topk(lg, topk, rids, rw)  # noqa: E731
+            us = timed(torch, callr, max(20, args.steps), min(args.warmup, 20), stream) * 1e3
+            rb = T * E * 4 + T * topk * 8
+            out["moe_route"] = {"T": T, "E": E, "topk": topk, "us": round(us, 2),
+                                "GBps": round(rb / us / 1e3, 1)}
+            del lg, rids, rw
         # decode-sized calls (the swap-AB kernels): the first Td tokens of the
         # same inputs; the call streams the weights of the experts they name
         dec = []
@@ -370,6 +381,7 @@ def main():
         "moe": out.get("moe"),
         "moe_decode": out.get("moe_decode"),
         "moe_nvfp4": out.get("moe_nvfp4"),
+        "moe_route": out.get("moe_route"),
         "device": torch.cuda.get_device_properties(0).gcnArchName,
         "kernel_src": src_hash("gemm_w4a4.hip", "common.h"),
     }

@@ -74,6 +74,7 @@ def load() -> C.CDLL:
                                       vp, vp, C.c_size_t, vp, vp]),
         "mgemm_moe_nvfp4_glu": (i32, [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, vp, vp,
                                       vp, vp, vp, vp, vp, vp, C.c_size_t, vp, vp]),
+        "mgemm_moe_route_topk": (i32, [vp, i64, i64, i64, vp, vp, vp]),
         "mgemm_workspace_bytes": (C.c_size_t, [i32, i64, i64, i64, i64, i64, i64, i64, i64]),
         "mgemm_status_string": (C.c_char_p, [i32]),
         "mgemm_version": (C.c_char_p, []),
@@ -311,3 +312,18 @@ def mgemm_moe_nvfp4_glu(xq, xs, Sx, topk_ids, topk_w, w13q, w13s, Sw13, w2q, w2s
         ws.numel() * ws.element_size(), dbg_h.data_ptr() if dbg_h is not None else None,
         _stream(stream)))
     return out
+
+
+def mgemm_moe_route_topk(logits, topk, topk_ids=None, topk_w=None, stream=None):
+    """(ids int32 [T,topk], weights FP32 [T,topk]) from FP32 router logits [T,E]."""
+    T, E = logits.shape
+    _need(logits, "logits", _F32, (T, E))
+    if topk_ids is None:
+        topk_ids = torch.empty((T, topk), dtype=torch.int32, device=logits.device)
+    if topk_w is None:
+        topk_w = torch.empty((T, topk), dtype=torch.float32, device=logits.device)
+    _need(topk_ids, "topk_ids", (torch.int32,), (T, topk))
+    _need(topk_w, "topk_w", _F32, (T, topk))
+    _check("mgemm_moe_route_topk", load().mgemm_moe_route_topk(
+        logits.data_ptr(), T, E, topk, topk_ids.data_ptr(), topk_w.data_ptr(), _stream(stream)))
+    return topk_ids, topk_w

@@ -257,6 +257,18 @@ int mgemm_moe_nvfp4_glu(const void *xq, const void *xs, const float *Sx,
   return finish(mg::launch_moe4(p, (hipStream_t)stream), "mgemm_moe_nvfp4_glu");
 }
 
+int mgemm_moe_route_topk(const float *logits, int64_t T, int64_t E, int64_t topk,
+                         int32_t *topk_ids, float *topk_w, void *stream) {
+  if (!logits || !topk_ids || !topk_w) return MGEMM_ERR_INVALID_ARG;
+  if (((uintptr_t)logits & 3) || ((uintptr_t)topk_ids & 3) || ((uintptr_t)topk_w & 3))
+    return MGEMM_ERR_INVALID_ARG;
+  if (T <= 0 || E <= 0 || topk <= 0 || topk > E || E > 1024 || T > (1 << 24))
+    return MGEMM_ERR_SHAPE;
+  return finish(mg::launch_topk_softmax(logits, (int)T, (int)E, (int)topk, topk_ids, topk_w,
+                                        (hipStream_t)stream),
+                "mgemm_moe_route_topk");
+}
+
 size_t mgemm_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int64_t T, int64_t H,
                              int64_t I, int64_t E, int64_t topk) {
   switch (op) {

@@ -81,6 +81,9 @@ struct Moe4Args {
   uint8_t *dbg_h;   // optional: per entry, I/2 code bytes then I/16 scale bytes
 };
 size_t moe4_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk);
+// router top-k: ids / weights [T, topk] from FP32 logits [T, E] (E <= 1024)
+hipError_t launch_topk_softmax(const float *logits, int T, int E, int topk, int32_t *ids,
+                               float *w, hipStream_t stream);
 hipError_t launch_moe4(const Moe4Args &p, hipStream_t stream);
 // the grouped W4A4 GEMMs of the NVFP4 MoE (moe4.hip), on the routing that
 // launch_moe4 (moe.hip) has written to the workspace

@@ -696,6 +696,70 @@ __global__ __launch_bounds__(256) void k_dec(MoeArgs p, const int32_t *meta, con
   }
 }
 
+// Router top-k (softmax of the logits, the k largest, as the MoE
+// configuration routes): one wave per token, expert e in lane e % 64,
+// register e / 64.  The softmax is taken in FP32 (max, exp, a butterfly sum
+// that leaves every lane the same value, one division per weight); the k
+// experts are chosen on the logits, which orders them as the exact
+// probabilities (equal logits: the lower id first).
+template <int PER>
+__global__ __launch_bounds__(256) void k_topk_softmax(const float *logits, int T, int E, int topk,
+                                                      int32_t *ids, float *w) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float *row = logits + (int64_t)t * E;
+  float v[PER], ex[PER];
+  float m = -__builtin_inff();
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int e = lane + 64 * q;
+    v[q] = e < E ? row[e] : -__builtin_inff();
+    m = fmaxf(m, v[q]);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  float s = 0.0f;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    ex[q] = lane + 64 * q < E ? expf(v[q] - m) : 0.0f;
+    s += ex[q];
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+  for (int j = 0; j < topk; ++j) {
+    // the largest remaining logit, lowest id on equal values
+    float bv = -__builtin_inff();
+    int be = 0x7FFFFFFF;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int e = lane + 64 * q;
+      if (e < E && (v[q] > bv || (v[q] == bv && e < be))) {
+        bv = v[q];
+        be = e;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, 64);
+      const int oe = __shfl_xor(be, o, 64);
+      if (ov > bv || (ov == bv && oe < be)) {
+        bv = ov;
+        be = oe;
+      }
+    }
+    if (lane == (be & 63)) {
+#pragma unroll
+      for (int q = 0; q < PER; ++q)
+        if (q == be >> 6) {
+          ids[(int64_t)t * topk + j] = be;
+          w[(int64_t)t * topk + j] = ex[q] / s;
+          v[q] = -__builtin_inff();   // taken (finite logits: never chosen again)
+        }
+    }
+  }
+}
+
 // one thread per (token, 4 columns): slots summed in order 0..topk-1; every
 // slot's row index, then every row, is requested before the first add
 __global__ void k_combine(const float *y, const int32_t *pos, int T, int H, int topk,
@@ -897,6 +961,22 @@ hipError_t launch_moe4(const Moe4Args &p, hipStream_t stream) {
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_combine, dim3((unsigned)((TH4 + 255) / 256)), dim3(256), 0, stream, y,
                      pos, p.T, p.H, p.topk, p.out);
+  return hipGetLastError();
+}
+
+}  // namespace mg
+
+namespace mg {
+
+hipError_t launch_topk_softmax(const float *logits, int T, int E, int topk, int32_t *ids,
+                               float *w, hipStream_t stream) {
+  const dim3 grid((unsigned)((T + 3) / 4)), block(256);
+  if (E <= 64)
+    hipLaunchKernelGGL(k_topk_softmax<1>, grid, block, 0, stream, logits, T, E, topk, ids, w);
+  else if (E <= 256)
+    hipLaunchKernelGGL(k_topk_softmax<4>, grid, block, 0, stream, logits, T, E, topk, ids, w);
+  else
+    hipLaunchKernelGGL(k_topk_softmax<16>, grid, block, 0, stream, logits, T, E, topk, ids, w);
   return hipGetLastError();
 }
 

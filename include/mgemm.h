@@ -219,6 +219,18 @@ int mgemm_moe_nvfp4_glu(const void *xq, const void *xs, const float *Sx,
                         const void *w2s, const float *Sw2, const float *Sh, void *out,
                         void *ws, size_t ws_bytes, void *dbg_h, void *stream);
 
+/* Router top-k of the MoE configuration (top-k routing from the softmax of
+   the router logits; FlashInfer skill page's MoE, the survey's workload of
+   64 experts, top 8).  logits: [T,E] FP32, finite.  Per token: p =
+   softmax(logits) in FP32; topk_ids[t,0..topk) = the topk experts of largest
+   p in descending order (chosen on the logits, which is the order of the
+   exact probabilities; equal logits: the lower id first); topk_w = those p,
+   not renormalised.  Outputs [T,topk] int32 / FP32, the inputs of the MoE
+   entry points.  E in [1,1024], topk in [1,E], T <= 2^24; device pointers,
+   4-byte aligned. */
+int mgemm_moe_route_topk(const float *logits, int64_t T, int64_t E, int64_t topk,
+                         int32_t *topk_ids, float *topk_w, void *stream);
+
 /* workspace sizes */
 enum { MGEMM_OP_BF16 = 0, MGEMM_OP_W4A16 = 1, MGEMM_OP_W4A8 = 2, MGEMM_OP_W4A4 = 3,
        MGEMM_OP_MOE = 4, MGEMM_OP_MOE_NVFP4 = 5 };

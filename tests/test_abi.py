@@ -102,6 +102,9 @@ def test_workspace_sizes(lib):
     assert mg.mgemm_workspace_bytes(mg.OP_MOE, T=4096, H=4096, I=1500, E=64, topk=8) == 0
     assert mg.mgemm_workspace_bytes(mg.OP_W4A8, 1, 5376, 100) == 0  # invalid K
     assert mg.mgemm_workspace_bytes(99, 1, 1, 32) == 0
+    moe4 = mg.mgemm_workspace_bytes(mg.OP_MOE_NVFP4, T=4096, H=4096, I=1536, E=64, topk=8)
+    assert moe4 > 4096 * 8 * 4096 * 4 + 4096 * 8 * (1536 // 2 + 1536 // 16)
+    assert mg.mgemm_workspace_bytes(mg.OP_MOE_NVFP4, T=4096, H=4096, I=1504, E=64, topk=8) == 0
 
 
 def test_host_side_argument_errors(lib):
@@ -127,6 +130,20 @@ def test_host_side_argument_errors(lib):
     assert moe(E=0) == -2
     assert lib.mgemm_moe_mxfp8_glu(p, p, None, p, 64, 128, 128, 4, 2, p, p, p, p, p, p,
                                    1 << 30, None, None) == -1
+    moe4 = lambda **kw: lib.mgemm_moe_nvfp4_glu(  # noqa: E731
+        p, p, kw.get("Sx", p), p, p, kw.get("T", 64), kw.get("H", 128), kw.get("I", 128),
+        kw.get("E", 4), kw.get("topk", 2), p, p, p, p, p, p, p, p, p, 1 << 30, None, None)
+    assert moe4(H=48) == -2          # H % 32
+    assert moe4(I=96) == -2          # I % 64
+    assert moe4(topk=17) == -2
+    assert moe4(T=0) == -2
+    assert moe4(Sx=None) == -1
+    assert moe4(Sx=p + 2) == -1      # FP32 scale not 4-byte aligned
+    assert lib.mgemm_moe_route_topk(None, 8, 64, 8, p, p, None) == -1
+    assert lib.mgemm_moe_route_topk(p, 8, 64, 65, p, p, None) == -2    # topk > E
+    assert lib.mgemm_moe_route_topk(p, 8, 1025, 8, p, p, None) == -2   # E > 1024
+    assert lib.mgemm_moe_route_topk(p, 0, 64, 8, p, p, None) == -2
+    assert lib.mgemm_moe_route_topk(p + 2, 8, 64, 8, p, p, None) == -1
 
 
 def test_binding_refuses_cpu_tensors(lib):
