@@ -29,7 +29,6 @@ namespace {
 
 constexpr int BM = 256, BN = 128, BK = 64;
 constexpr int NTHR = 512;            // 8 waves
-constexpr int NSTAGE = 3;            // LDS ring depth
 constexpr int ROWB = BK * 2;         // bytes per LDS row (64 BF16)
 constexpr int STAGE_A = BM * ROWB, STAGE_W = BN * ROWB;
 

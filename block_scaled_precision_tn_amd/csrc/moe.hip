@@ -370,7 +370,7 @@ __global__ __launch_bounds__(256) void k_gateup(MoeArgs p, const int32_t *meta,
   const int e = tile_e[tile], r0 = tile_r[tile], nrows = tile_n[tile];
   const int i0 = blockIdx.x * BNI;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1, h = lane >> 5, l32 = lane & 31;
+  const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31;
   const int H = p.H, I = p.I;
 
   // A rows: gathered token rows (rows past the tile read the first entry's
