@@ -244,7 +244,20 @@ def main():
         out["bf16"] = {"M": Mb, "N": N, "K": K, "ms": round(ms, 4), "tflops": round(tf, 1),
                        "frac_bf16_peak": round(tf / PEAK["bf16"], 4),
                        "torch_matmul_tflops": round(tf_t, 1)}
-        del A, W, Cb
+        # its backward: dX = dY . W (A doubles as dX's shape donor), dW = dY^T . X
+        dY = Cb.normal_()
+        dX = torch.empty((Mb, K), dtype=torch.bfloat16, device=dev)
+        dW = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+        ms_d = timed(torch, lambda i: mg.mgemm_bf16_dgrad(dY, W, dX), max(5, args.steps // 4),
+                     min(args.warmup, 10), stream)
+        ms_w = timed(torch, lambda i: mg.mgemm_bf16_wgrad(dY, A, dW), max(5, args.steps // 4),
+                     min(args.warmup, 10), stream)
+        fl = 2.0 * Mb * N * K
+        out["bf16_grad"] = {"M": Mb, "N": N, "K": K, "dgrad_ms": round(ms_d, 4),
+                            "dgrad_tflops": round(fl / (ms_d * 1e-3) / 1e12, 1),
+                            "wgrad_ms": round(ms_w, 4),
+                            "wgrad_tflops": round(fl / (ms_w * 1e-3) / 1e12, 1)}
+        del A, W, Cb, dY, dX, dW
         torch.cuda.empty_cache()
 
     # ------------------------------------------------------------------- MoE
@@ -378,6 +391,7 @@ def main():
         "parity_sample": par,
         "decode": out.get("decode"),
         "bf16": out.get("bf16"),
+        "bf16_grad": out.get("bf16_grad"),
         "moe": out.get("moe"),
         "moe_decode": out.get("moe_decode"),
         "moe_nvfp4": out.get("moe_nvfp4"),

@@ -32,6 +32,7 @@ FMT_BF16, FMT_NVFP4, FMT_FP8_E4M3_TOKEN, FMT_MXFP8 = 0, 1, 2, 3
 EXEC_NATIVE, EXEC_FP8_EXACT, EXEC_NOPATH = 0, 1, 2
 MMA_NONE, MMA_BF16, MMA_FP8, MMA_MX_F8F6F4 = 0, 1, 2, 3
 OP_BF16, OP_W4A16, OP_W4A8, OP_W4A4, OP_MOE, OP_MOE_NVFP4 = 0, 1, 2, 3, 4, 5
+OP_BF16_DGRAD, OP_BF16_WGRAD = 6, 7
 
 EXEC_NAMES = {EXEC_NATIVE: "native", EXEC_FP8_EXACT: "fp8_exact", EXEC_NOPATH: "nopath"}
 MMA_NAMES = {MMA_NONE: "none", MMA_BF16: "bf16", MMA_FP8: "fp8", MMA_MX_F8F6F4: "mx_f8f6f4"}
@@ -75,6 +76,8 @@ def load() -> C.CDLL:
         "mgemm_moe_nvfp4_glu": (i32, [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, vp, vp,
                                       vp, vp, vp, vp, vp, vp, C.c_size_t, vp, vp]),
         "mgemm_moe_route_topk": (i32, [vp, i64, i64, i64, vp, vp, vp]),
+        "mgemm_bf16_dgrad": (i32, [vp, vp, vp, i64, i64, i64, i32, vp, C.c_size_t, vp]),
+        "mgemm_bf16_wgrad": (i32, [vp, vp, vp, i64, i64, i64, i32, vp, C.c_size_t, vp]),
         "mgemm_workspace_bytes": (C.c_size_t, [i32, i64, i64, i64, i64, i64, i64, i64, i64]),
         "mgemm_status_string": (C.c_char_p, [i32]),
         "mgemm_version": (C.c_char_p, []),
@@ -327,3 +330,41 @@ def mgemm_moe_route_topk(logits, topk, topk_ids=None, topk_w=None, stream=None):
     _check("mgemm_moe_route_topk", load().mgemm_moe_route_topk(
         logits.data_ptr(), T, E, topk, topk_ids.data_ptr(), topk_w.data_ptr(), _stream(stream)))
     return topk_ids, topk_w
+
+
+def mgemm_bf16_dgrad(dY, W, dX=None, out_f32=False, ws: Optional[torch.Tensor] = None, stream=None):
+    """dX[M,K] = dY[M,N] . W[N,K] (BF16 in, BF16 or FP32 out)."""
+    M, N = dY.shape
+    _, K = W.shape
+    _need(dY, "dY", (torch.bfloat16,), (M, N))
+    _need(W, "W", (torch.bfloat16,), (N, K))
+    if dX is None:
+        dX = torch.empty((M, K), dtype=torch.float32 if out_f32 else torch.bfloat16, device=dY.device)
+    _need(dX, "dX", (torch.float32 if out_f32 else torch.bfloat16,), (M, K))
+    need = mgemm_workspace_bytes(OP_BF16_DGRAD, M, N, K)
+    if ws is None:
+        ws = workspace(need, "bf16_dgrad")
+    _check("mgemm_bf16_dgrad", load().mgemm_bf16_dgrad(
+        dY.data_ptr(), W.data_ptr(), dX.data_ptr(), M, N, K, int(out_f32),
+        ws.data_ptr() if ws is not None else None,
+        ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream)))
+    return dX
+
+
+def mgemm_bf16_wgrad(dY, X, dW=None, out_f32=False, ws: Optional[torch.Tensor] = None, stream=None):
+    """dW[N,K] = dY[M,N]^T . X[M,K] (BF16 in, BF16 or FP32 out)."""
+    M, N = dY.shape
+    _, K = X.shape
+    _need(dY, "dY", (torch.bfloat16,), (M, N))
+    _need(X, "X", (torch.bfloat16,), (M, K))
+    if dW is None:
+        dW = torch.empty((N, K), dtype=torch.float32 if out_f32 else torch.bfloat16, device=dY.device)
+    _need(dW, "dW", (torch.float32 if out_f32 else torch.bfloat16,), (N, K))
+    need = mgemm_workspace_bytes(OP_BF16_WGRAD, M, N, K)
+    if ws is None:
+        ws = workspace(need, "bf16_wgrad")
+    _check("mgemm_bf16_wgrad", load().mgemm_bf16_wgrad(
+        dY.data_ptr(), X.data_ptr(), dW.data_ptr(), M, N, K, int(out_f32),
+        ws.data_ptr() if ws is not None else None,
+        ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream)))
+    return dW

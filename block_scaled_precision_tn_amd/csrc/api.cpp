@@ -257,6 +257,34 @@ int mgemm_moe_nvfp4_glu(const void *xq, const void *xs, const float *Sx,
   return finish(mg::launch_moe4(p, (hipStream_t)stream), "mgemm_moe_nvfp4_glu");
 }
 
+int mgemm_bf16_dgrad(const void *dY, const void *W, void *dX, int64_t M, int64_t N, int64_t K,
+                     int out_f32, void *ws, size_t ws_bytes, void *stream) {
+  if (!dY || !W || !dX || (out_f32 != 0 && out_f32 != 1)) return MGEMM_ERR_INVALID_ARG;
+  if (!aligned16(dY) || !aligned16(W) || !aligned16(dX)) return MGEMM_ERR_INVALID_ARG;
+  if (int rc = check_mnk(M, K, N)) return rc;            // contraction over N
+  if (K % 8 != 0) return MGEMM_ERR_SHAPE;
+  if (int rc = check_path(MGEMM_FMT_BF16, MGEMM_FMT_BF16)) return rc;
+  if (!ws || !aligned16(ws) || ws_bytes < mg::bf16_grad_workspace_bytes(false, M, N, K))
+    return MGEMM_ERR_WORKSPACE;
+  return finish(mg::launch_bf16_dgrad((const uint16_t *)dY, (const uint16_t *)W, dX, (int)M,
+                                      (int)N, (int)K, out_f32, ws, (hipStream_t)stream),
+                "mgemm_bf16_dgrad");
+}
+
+int mgemm_bf16_wgrad(const void *dY, const void *X, void *dW, int64_t M, int64_t N, int64_t K,
+                     int out_f32, void *ws, size_t ws_bytes, void *stream) {
+  if (!dY || !X || !dW || (out_f32 != 0 && out_f32 != 1)) return MGEMM_ERR_INVALID_ARG;
+  if (!aligned16(dY) || !aligned16(X) || !aligned16(dW)) return MGEMM_ERR_INVALID_ARG;
+  if (int rc = check_mnk(N, K, M)) return rc;            // contraction over M
+  if (N % 8 != 0 || K % 8 != 0) return MGEMM_ERR_SHAPE;
+  if (int rc = check_path(MGEMM_FMT_BF16, MGEMM_FMT_BF16)) return rc;
+  if (!ws || !aligned16(ws) || ws_bytes < mg::bf16_grad_workspace_bytes(true, M, N, K))
+    return MGEMM_ERR_WORKSPACE;
+  return finish(mg::launch_bf16_wgrad((const uint16_t *)dY, (const uint16_t *)X, dW, (int)M,
+                                      (int)N, (int)K, out_f32, ws, (hipStream_t)stream),
+                "mgemm_bf16_wgrad");
+}
+
 int mgemm_moe_route_topk(const float *logits, int64_t T, int64_t E, int64_t topk,
                          int32_t *topk_ids, float *topk_w, void *stream) {
   if (!logits || !topk_ids || !topk_w) return MGEMM_ERR_INVALID_ARG;
@@ -284,6 +312,12 @@ size_t mgemm_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int64_t T,
           H % 64 != 0 || I % 64 != 0)
         return 0;
       return mg::moe_workspace_bytes(T, H, I, E, topk);
+    case MGEMM_OP_BF16_DGRAD:
+      if (check_mnk(M, K, N) != MGEMM_OK || K % 8 != 0) return 0;
+      return mg::bf16_grad_workspace_bytes(false, M, N, K);
+    case MGEMM_OP_BF16_WGRAD:
+      if (check_mnk(N, K, M) != MGEMM_OK || N % 8 != 0 || K % 8 != 0) return 0;
+      return mg::bf16_grad_workspace_bytes(true, M, N, K);
     case MGEMM_OP_MOE_NVFP4:
       if (T <= 0 || H <= 0 || I <= 0 || E <= 0 || topk <= 0 || topk > 16 || E > 1024 ||
           H % 32 != 0 || I % 64 != 0)

@@ -30,6 +30,13 @@ struct Bf16Args {
   int w_nvfp4;
 };
 hipError_t launch_bf16(const Bf16Args &p, hipStream_t stream);
+// backward of y = x . W^T (grad_bf16.hip): operands transposed into the
+// workspace, then the TN kernel
+size_t bf16_grad_workspace_bytes(bool wgrad, int64_t M, int64_t N, int64_t K);
+hipError_t launch_bf16_dgrad(const uint16_t *dY, const uint16_t *W, void *dX, int M, int N, int K,
+                             int out_f32, void *ws, hipStream_t stream);
+hipError_t launch_bf16_wgrad(const uint16_t *dY, const uint16_t *X, void *dW, int M, int N, int K,
+                             int out_f32, void *ws, hipStream_t stream);
 
 struct W4A8Args {
   const uint8_t *aq;

@@ -231,9 +231,25 @@ int mgemm_moe_nvfp4_glu(const void *xq, const void *xs, const float *Sx,
 int mgemm_moe_route_topk(const float *logits, int64_t T, int64_t E, int64_t topk,
                          int32_t *topk_ids, float *topk_w, void *stream);
 
+/* Backward of the BF16 FFN down projection y = x . W^T (RL-Kernel PR #535's
+   H3 operator; its backward names dY . W as the input gradient):
+     dgrad: dX[M,K] = dY[M,N] . W[N,K]       (sum over N)
+     wgrad: dW[N,K] = dY[M,N]^T . X[M,K]     (sum over M)
+   BF16 operands, row-major, FP32 accumulation, BF16 output (FP32 with
+   out_f32 = 1).  Each output's sum runs in one fixed order: run-to-run
+   bit-identical.  ws: at least mgemm_workspace_bytes(MGEMM_OP_BF16_DGRAD /
+   _WGRAD, M, N, K) bytes (the operands written contraction-major: W^T, or
+   dY^T and X^T), no particular contents.  The contraction (N for dgrad, M
+   for wgrad) must be a multiple of 32, K (and N for wgrad) a multiple of 8. */
+int mgemm_bf16_dgrad(const void *dY, const void *W, void *dX, int64_t M, int64_t N, int64_t K,
+                     int out_f32, void *ws, size_t ws_bytes, void *stream);
+int mgemm_bf16_wgrad(const void *dY, const void *X, void *dW, int64_t M, int64_t N, int64_t K,
+                     int out_f32, void *ws, size_t ws_bytes, void *stream);
+
 /* workspace sizes */
 enum { MGEMM_OP_BF16 = 0, MGEMM_OP_W4A16 = 1, MGEMM_OP_W4A8 = 2, MGEMM_OP_W4A4 = 3,
-       MGEMM_OP_MOE = 4, MGEMM_OP_MOE_NVFP4 = 5 };
+       MGEMM_OP_MOE = 4, MGEMM_OP_MOE_NVFP4 = 5, MGEMM_OP_BF16_DGRAD = 6,
+       MGEMM_OP_BF16_WGRAD = 7 };
 /* Bytes of device workspace an op needs for these sizes (0 if none).  For the
    GEMMs pass (M, N, K) and zeros; for the MoE pass (T, H, I, E, topk) in the
    T.. arguments.  Returns 0 for unknown ops or invalid sizes as well. */
