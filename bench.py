@@ -286,22 +286,28 @@ def main():
             out["moe_route"] = {"T": T, "E": E, "topk": topk, "us": round(us, 2),
                                 "GBps": round(rb / us / 1e3, 1)}
             del lg, rids, rw
-        # decode-sized calls (the swap-AB kernels): the first Td tokens of the
-        # same inputs; the call streams the weights of the experts they name
+        # decode-sized calls (the swap-AB kernels): successive calls take
+        # successive groups of Td tokens of the same inputs, so they name
+        # different experts and the weights they stream (1.25 GB in all) do
+        # not stay in the 256 MB Infinity Cache between calls
         dec = []
         for Td in [int(v) for v in args.moe_dec_tokens.split(",") if v] if args.only != "moe" else []:
-            sl = {k: dm[k][:Td].contiguous() for k in ("xq", "xs", "ids", "tw")}
+            groups = max(1, min(16, T // Td))
+            sls = [{k: dm[k][g * Td:(g + 1) * Td].contiguous() for k in ("xq", "xs", "ids", "tw")}
+                   for g in range(groups)]
             od = torch.empty((Td, H), dtype=torch.bfloat16, device=dev)
             wsd = mg.workspace(mg.mgemm_workspace_bytes(mg.OP_MOE, T=Td, H=H, I=I, E=E, topk=topk),
                                "moe_dec")
-            calld = lambda i, sl=sl, od=od, wsd=wsd: mg.mgemm_moe_mxfp8_glu(  # noqa: E731
-                sl["xq"], sl["xs"], sl["ids"], sl["tw"], dm["w13q"], dm["w13s"], dm["w2q"],
-                dm["w2s"], od, ws=wsd)
-            us = timed(torch, calld, max(20, args.steps), min(args.warmup, 20), stream) * 1e3
-            ne = len(np.unique(m["ids"][:Td]))
+            calld = lambda i, sls=sls, od=od, wsd=wsd: mg.mgemm_moe_mxfp8_glu(  # noqa: E731
+                sls[i % len(sls)]["xq"], sls[i % len(sls)]["xs"], sls[i % len(sls)]["ids"],
+                sls[i % len(sls)]["tw"], dm["w13q"], dm["w13s"], dm["w2q"], dm["w2s"], od, ws=wsd)
+            steps_d = len(sls) * max(1, max(20, args.steps) // len(sls))
+            us = timed(torch, calld, steps_d, min(args.warmup, 20), stream) * 1e3
+            ne = np.mean([len(np.unique(m["ids"][g * Td:(g + 1) * Td])) for g in range(groups)])
             nbytes = (ne * 3 * I * H * (1 + 1 / 32)                  # expert weights, codes + scales
                       + Td * H * (1 + 1 / 32) + Td * topk * 8 + 2 * Td * H)   # x, routing, out
-            dec.append({"T": Td, "experts": ne, "us": round(us, 2), "bytes": int(nbytes),
+            dec.append({"T": Td, "experts": round(float(ne), 2), "token_groups": groups,
+                        "us": round(us, 2), "bytes": int(nbytes),
                         "GBps": round(nbytes / us / 1e3, 1),
                         "frac_hbm": round(nbytes / us / 1e3 / PEAK["hbm"], 4)})
         out["moe_decode"] = dec
