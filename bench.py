@@ -186,8 +186,8 @@ def main():
         # multiply-add per output per 16-element group (the group-scale step),
         # M*N*K/16 per launch, against the MFMA work of 2 FP8 MFMAs per 32x32
         # block and group.  `roofline` is that ALU work against the published
-        # FP32 vector peak (which counts packed FP32 instructions; this build
-        # emits none, so 78.6 TFLOP/s is the attainable half); `mfma_roofline`
+        # FP32 vector peak (which counts packed FP32 instructions; these
+        # kernels emit none, so 78.6 TFLOP/s is the attainable half); `mfma_roofline`
         # the GEMM flops against the FP8 MFMA peak (the metric's "% MFMA peak").
         alu = 2.0 * groups / (ms * 1e-3) / 1e12
         out["roofline"] = {"bound": "alu", "achieved": round(alu, 2), "peak": PEAK["fp32"],

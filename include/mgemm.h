@@ -219,9 +219,9 @@ int mgemm_moe_nvfp4_glu(const void *xq, const void *xs, const float *Sx,
                         const void *w2s, const float *Sw2, const float *Sh, void *out,
                         void *ws, size_t ws_bytes, void *dbg_h, void *stream);
 
-/* Router top-k of the MoE configuration (top-k routing from the softmax of
-   the router logits; FlashInfer skill page's MoE, the survey's workload of
-   64 experts, top 8).  logits: [T,E] FP32, finite.  Per token: p =
+/* Router top-k of the MoE (top-k routing from the softmax of the router
+   logits, as the mixture-of-experts GLUs above are fed; e.g. 64 experts,
+   top 8).  logits: [T,E] FP32, finite.  Per token: p =
    softmax(logits) in FP32; topk_ids[t,0..topk) = the topk experts of largest
    p in descending order (chosen on the logits, which is the order of the
    exact probabilities; equal logits: the lower id first); topk_w = those p,
