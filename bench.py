@@ -44,7 +44,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quick", action="store_true", help="headline kernel only")
     ap.add_argument("--only", default="",
-                    help="w4a4|w4a8|bf16|moe|moe_decode|moe_nvfp4 (profiling runs)")
+                    help="w4a4|w4a8|bf16|bf16_grad|moe|moe_decode|moe_nvfp4 (profiling runs)")
     ap.add_argument("--moe-dec-tokens", default="1,16",
                     help="token counts of the decode-sized MoE calls")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -231,19 +231,20 @@ def main():
         torch.cuda.empty_cache()
 
     # ------------------------------------------------------------------ BF16
-    if args.only in ("", "bf16") and not args.quick:
+    if args.only in ("", "bf16", "bf16_grad") and not args.quick:
         Mb = 4096
         b = synth.bf16(Mb, N, K, seed=0)
         A = todev(b["a"].view(np.int16)).view(torch.bfloat16)
         W = todev(b["w"].view(np.int16)).view(torch.bfloat16)
         Cb = torch.empty((Mb, N), dtype=torch.bfloat16, device=dev)
-        ms = timed(torch, lambda i: mg.mgemm_bf16(A, W, Cb), args.steps, args.warmup, stream)
-        tf = 2.0 * Mb * N * K / (ms * 1e-3) / 1e12
-        ms_t = timed(torch, lambda i: torch.matmul(A, W.t()), args.steps, args.warmup, stream)
-        tf_t = 2.0 * Mb * N * K / (ms_t * 1e-3) / 1e12
-        out["bf16"] = {"M": Mb, "N": N, "K": K, "ms": round(ms, 4), "tflops": round(tf, 1),
-                       "frac_bf16_peak": round(tf / PEAK["bf16"], 4),
-                       "torch_matmul_tflops": round(tf_t, 1)}
+        if args.only != "bf16_grad":
+            ms = timed(torch, lambda i: mg.mgemm_bf16(A, W, Cb), args.steps, args.warmup, stream)
+            tf = 2.0 * Mb * N * K / (ms * 1e-3) / 1e12
+            ms_t = timed(torch, lambda i: torch.matmul(A, W.t()), args.steps, args.warmup, stream)
+            tf_t = 2.0 * Mb * N * K / (ms_t * 1e-3) / 1e12
+            out["bf16"] = {"M": Mb, "N": N, "K": K, "ms": round(ms, 4), "tflops": round(tf, 1),
+                           "frac_bf16_peak": round(tf / PEAK["bf16"], 4),
+                           "torch_matmul_tflops": round(tf_t, 1)}
         # its backward: dX = dY . W (A doubles as dX's shape donor), dW = dY^T . X
         dY = Cb.normal_()
         dX = torch.empty((Mb, K), dtype=torch.bfloat16, device=dev)
