@@ -155,6 +155,20 @@ def test_moe4_stagewise(T, H, I, E, topk):
     _check_down_combine(inp, d, out, T, H, I, topk, tokens)
 
 
+def test_moe4_skewed_routing_and_empty_experts():
+    """Half the experts get no tokens, one gets most (several 128-row tiles)."""
+    T, H, I, E, topk = 200, 128, 128, 8, 2
+    inp = synth.moe_nvfp4(T, H, I, E, topk, seed=5)
+    rng = np.random.default_rng(5)
+    ids = np.where(rng.random((T, topk)) < 0.8, 3, rng.integers(0, 4, (T, topk))).astype(np.int32)
+    ids[:, 1] = np.where(ids[:, 1] == ids[:, 0], (ids[:, 0] + 1) % 4, ids[:, 1])
+    inp["ids"] = ids
+    out, d = run_moe4(inp, T, H, I, E, topk)
+    tokens = np.arange(0, T, 3)
+    _check_requant(inp, d, T, H, I, topk, tokens)
+    _check_down_combine(inp, d, out, T, H, I, topk, tokens)
+
+
 def test_moe4_repeat_bit_identical():
     T, H, I, E, topk = 64, 256, 128, 8, 4
     inp = synth.moe_nvfp4(T, H, I, E, topk, seed=9)

@@ -39,7 +39,7 @@ def route(lg, k):
 
 @pytest.mark.parametrize("T,E,k,rtol", [(4096, 64, 8, 1e-5), (37, 1000, 13, 2e-5),
                                         (130, 256, 1, 1e-5), (5, 64, 64, 1e-5),
-                                        (9, 7, 3, 1e-5)])
+                                        (9, 7, 3, 1e-5), (3, 1, 1, 1e-5)])
 def test_route_matches_oracle(T, E, k, rtol):
     lg = synth.moe_logits(T, E, seed=T + E)
     ids, w = route(lg, k)
