@@ -73,6 +73,10 @@ def load() -> C.CDLL:
         "mgemm_w4a4": (i32, [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]),
         "mgemm_moe_mxfp8_glu": (i32, [vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, vp, vp, vp,
                                       vp, vp, C.c_size_t, vp, vp]),
+        "mgemm_moe_mxfp8_glu_debug": (i32, [vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, vp, vp,
+                                            vp, vp, vp, C.c_size_t, vp, vp, vp]),
+        "mgemm_moe_mxfp8_glu_logits": (i32, [vp, vp, vp, i64, i64, i64, i64, i64, vp, vp, vp, vp,
+                                             vp, vp, vp, vp, C.c_size_t, vp, vp]),
         "mgemm_moe_nvfp4_glu": (i32, [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, vp, vp,
                                       vp, vp, vp, vp, vp, vp, C.c_size_t, vp, vp]),
         "mgemm_moe_route_topk": (i32, [vp, i64, i64, i64, vp, vp, vp]),
@@ -194,16 +198,22 @@ def mgemm_w4a16(A, Wq, Ws, Sw, C_out, stream=None):
 _WS_CACHE = {}
 
 
-def workspace(nbytes: int, key=None) -> Optional[torch.Tensor]:
-    """A device workspace of at least nbytes, cached per device and key (grown
-    on demand).  Calls that share one must be ordered on one stream."""
+def workspace(nbytes: int, key=None, stream=None) -> Optional[torch.Tensor]:
+    """A device workspace of at least nbytes for work enqueued on `stream`
+    (None: the current stream), cached per (device, stream, key) and grown on
+    demand, so calls on different streams never share one.  The tensor is
+    marked as used by that stream: when a larger one replaces it, its memory
+    is not handed out again before the work already enqueued there is done."""
     if nbytes == 0:
         return None
     dev = torch.cuda.current_device()
-    k = (dev, key)
+    h = _stream(stream)
+    k = (dev, h, key)
     t = _WS_CACHE.get(k)
     if t is None or t.numel() < nbytes:
-        t = torch.zeros(nbytes, dtype=torch.uint8, device=f"cuda:{dev}")
+        t = torch.empty(nbytes, dtype=torch.uint8, device=f"cuda:{dev}")
+        if h != torch.cuda.current_stream().cuda_stream:
+            t.record_stream(torch.cuda.ExternalStream(h))
         _WS_CACHE[k] = t
     return t
 
@@ -219,7 +229,7 @@ def mgemm_w4a8(Aq, a_tok, Wq, Ws, Sw, C_out, ws: Optional[torch.Tensor] = None, 
     _need(C_out, "C", _C_T, (M, N))
     need = mgemm_workspace_bytes(OP_W4A8, M, N, K)
     if ws is None:
-        ws = workspace(need, "w4a8")
+        ws = workspace(need, "w4a8", stream)
     if need and (ws is None or ws.numel() * ws.element_size() < need):
         raise ValueError("w4a8: workspace too small")
     wp = ws.data_ptr() if ws is not None else None
@@ -250,7 +260,10 @@ def mgemm_w4a4(Aq, As, Sa, Wq, Ws, Sw, C_out, stream=None):
 
 def mgemm_moe_mxfp8_glu(xq, xs, topk_ids, topk_w, w13q, w13s, w2q, w2s, out,
                         ws: Optional[torch.Tensor] = None, dbg_h: Optional[torch.Tensor] = None,
-                        stream=None):
+                        stream=None, dbg_gu: Optional[torch.Tensor] = None):
+    """The MXFP8 MoE GLU.  dbg_h / dbg_gu: optional taps (uint8 [T*topk*(I +
+    I/32)], FP32 [T*topk*2I]); with dbg_gu the call goes through
+    mgemm_moe_mxfp8_glu_debug."""
     T, H = xq.shape
     topk = topk_ids.shape[1]
     E, I2, _ = w13q.shape
@@ -268,15 +281,61 @@ def mgemm_moe_mxfp8_glu(xq, xs, topk_ids, topk_w, w13q, w13s, w2q, w2s, out,
         _need(dbg_h, "dbg_h", _U8, numel=T * topk * (I + I // 32))
     need = mgemm_workspace_bytes(OP_MOE, T=T, H=H, I=I, E=E, topk=topk)
     if ws is None:
-        ws = workspace(need, "moe")
+        ws = workspace(need, "moe", stream)
     if ws.numel() * ws.element_size() < need:
         raise ValueError("moe: workspace too small")
+    if dbg_gu is not None:
+        _need(dbg_gu, "dbg_gu", _F32, numel=T * topk * 2 * I)
+        _check("mgemm_moe_mxfp8_glu_debug", load().mgemm_moe_mxfp8_glu_debug(
+            xq.data_ptr(), xs.data_ptr(), topk_ids.data_ptr(), topk_w.data_ptr(), T, H, I, E,
+            topk, w13q.data_ptr(), w13s.data_ptr(), w2q.data_ptr(), w2s.data_ptr(),
+            out.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(),
+            dbg_h.data_ptr() if dbg_h is not None else None, dbg_gu.data_ptr(), _stream(stream)))
+        return out
     _check("mgemm_moe_mxfp8_glu", load().mgemm_moe_mxfp8_glu(
         xq.data_ptr(), xs.data_ptr(), topk_ids.data_ptr(), topk_w.data_ptr(), T, H, I, E, topk,
         w13q.data_ptr(), w13s.data_ptr(), w2q.data_ptr(), w2s.data_ptr(), out.data_ptr(),
         ws.data_ptr(), ws.numel() * ws.element_size(),
         dbg_h.data_ptr() if dbg_h is not None else None, _stream(stream)))
     return out
+
+
+def mgemm_moe_mxfp8_glu_logits(xq, xs, logits, topk, w13q, w13s, w2q, w2s, out,
+                               topk_ids=None, topk_w=None, ws: Optional[torch.Tensor] = None,
+                               dbg_h: Optional[torch.Tensor] = None, stream=None):
+    """The MXFP8 MoE routed from FP32 router logits [T,E] in the same call
+    (softmax, top-k, expert counts in the route-prep launch).  Returns
+    (out, topk_ids, topk_w): the routing the call took, [T,topk]."""
+    T, H = xq.shape
+    E, I2, _ = w13q.shape
+    I = I2 // 2
+    _need(xq, "xq", _U8, (T, H))
+    _need(xs, "xs", _U8, (T, H // 32))
+    _need(logits, "logits", _F32, (T, E))
+    _need(w13q, "w13q", _U8, (E, 2 * I, H))
+    _need(w13s, "w13s", _U8, (E, 2 * I, H // 32))
+    _need(w2q, "w2q", _U8, (E, H, I))
+    _need(w2s, "w2s", _U8, (E, H, I // 32))
+    _need(out, "out", (torch.bfloat16,), (T, H))
+    if topk_ids is None:
+        topk_ids = torch.empty((T, topk), dtype=torch.int32, device=xq.device)
+    if topk_w is None:
+        topk_w = torch.empty((T, topk), dtype=torch.float32, device=xq.device)
+    _need(topk_ids, "topk_ids", (torch.int32,), (T, topk))
+    _need(topk_w, "topk_w", _F32, (T, topk))
+    if dbg_h is not None:
+        _need(dbg_h, "dbg_h", _U8, numel=T * topk * (I + I // 32))
+    need = mgemm_workspace_bytes(OP_MOE, T=T, H=H, I=I, E=E, topk=topk)
+    if ws is None:
+        ws = workspace(need, "moe", stream)
+    if ws.numel() * ws.element_size() < need:
+        raise ValueError("moe: workspace too small")
+    _check("mgemm_moe_mxfp8_glu_logits", load().mgemm_moe_mxfp8_glu_logits(
+        xq.data_ptr(), xs.data_ptr(), logits.data_ptr(), T, H, I, E, topk, w13q.data_ptr(),
+        w13s.data_ptr(), w2q.data_ptr(), w2s.data_ptr(), out.data_ptr(), topk_ids.data_ptr(),
+        topk_w.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(),
+        dbg_h.data_ptr() if dbg_h is not None else None, _stream(stream)))
+    return out, topk_ids, topk_w
 
 
 def mgemm_moe_nvfp4_glu(xq, xs, Sx, topk_ids, topk_w, w13q, w13s, Sw13, w2q, w2s, Sw2, Sh, out,
@@ -305,7 +364,7 @@ def mgemm_moe_nvfp4_glu(xq, xs, Sx, topk_ids, topk_w, w13q, w13s, Sw13, w2q, w2s
         _need(dbg_h, "dbg_h", _U8, numel=T * topk * (I // 2 + I // 16))
     need = mgemm_workspace_bytes(OP_MOE_NVFP4, T=T, H=H, I=I, E=E, topk=topk)
     if ws is None:
-        ws = workspace(need, "moe_nvfp4")
+        ws = workspace(need, "moe_nvfp4", stream)
     if ws.numel() * ws.element_size() < need:
         raise ValueError("moe_nvfp4: workspace too small")
     _check("mgemm_moe_nvfp4_glu", load().mgemm_moe_nvfp4_glu(
@@ -343,7 +402,7 @@ def mgemm_bf16_dgrad(dY, W, dX=None, out_f32=False, ws: Optional[torch.Tensor] =
     _need(dX, "dX", (torch.float32 if out_f32 else torch.bfloat16,), (M, K))
     need = mgemm_workspace_bytes(OP_BF16_DGRAD, M, N, K)
     if ws is None:
-        ws = workspace(need, "bf16_dgrad")
+        ws = workspace(need, "bf16_dgrad", stream)
     _check("mgemm_bf16_dgrad", load().mgemm_bf16_dgrad(
         dY.data_ptr(), W.data_ptr(), dX.data_ptr(), M, N, K, int(out_f32),
         ws.data_ptr() if ws is not None else None,
@@ -362,7 +421,7 @@ def mgemm_bf16_wgrad(dY, X, dW=None, out_f32=False, ws: Optional[torch.Tensor] =
     _need(dW, "dW", (torch.float32 if out_f32 else torch.bfloat16,), (N, K))
     need = mgemm_workspace_bytes(OP_BF16_WGRAD, M, N, K)
     if ws is None:
-        ws = workspace(need, "bf16_wgrad")
+        ws = workspace(need, "bf16_wgrad", stream)
     _check("mgemm_bf16_wgrad", load().mgemm_bf16_wgrad(
         dY.data_ptr(), X.data_ptr(), dW.data_ptr(), M, N, K, int(out_f32),
         ws.data_ptr() if ws is not None else None,

@@ -122,6 +122,33 @@ int finish(hipError_t e, const char *what) {
   return MGEMM_OK;
 }
 
+// the MXFP8 MoE entry points: routing ids / weights given (logits == NULL),
+// or routed from FP32 router logits, ids / weights then written by the call
+int moe_mxfp8(const void *xq, const void *xs, const float *logits, const int32_t *topk_ids,
+              const float *topk_w, int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk,
+              const void *w13q, const void *w13s, const void *w2q, const void *w2s, void *out,
+              void *ws, size_t ws_bytes, void *dbg_h, float *dbg_gu, void *stream,
+              const char *what) {
+  if (!xq || !xs || !topk_ids || !topk_w || !w13q || !w13s || !w2q || !w2s || !out)
+    return MGEMM_ERR_INVALID_ARG;
+  if (!aligned16(xq) || !aligned16(xs) || !aligned16(topk_ids) || !aligned16(topk_w) ||
+      !aligned16(w13q) || !aligned16(w13s) || !aligned16(w2q) || !aligned16(w2s) ||
+      !aligned16(out) || (dbg_h && !aligned16(dbg_h)) || (dbg_gu && !aligned16(dbg_gu)))
+    return MGEMM_ERR_INVALID_ARG;
+  if (T <= 0 || H <= 0 || I <= 0 || E <= 0 || topk <= 0) return MGEMM_ERR_SHAPE;
+  if (H % 64 != 0 || I % 64 != 0 || topk > 16 || E > 1024 || T > (1 << 24) ||
+      H > (1 << 20) || I > (1 << 20) || (double)T * topk * (double)(H > I ? H : I) > 4.0e18)
+    return MGEMM_ERR_SHAPE;
+  if (int rc = check_path(MGEMM_FMT_MXFP8, MGEMM_FMT_MXFP8)) return rc;
+  const size_t need = mg::moe_workspace_bytes(T, H, I, E, topk);
+  if (!ws || ws_bytes < need || !aligned16(ws)) return MGEMM_ERR_WORKSPACE;
+  mg::MoeArgs p{(const uint8_t *)xq, (const uint8_t *)xs, topk_ids, topk_w, (int)T, (int)H,
+                (int)I, (int)E, (int)topk, (const uint8_t *)w13q, (const uint8_t *)w13s,
+                (const uint8_t *)w2q, (const uint8_t *)w2s, (uint16_t *)out, ws, ws_bytes,
+                (uint8_t *)dbg_h, logits, dbg_gu};
+  return finish(mg::launch_moe(p, (hipStream_t)stream), what);
+}
+
 }  // namespace
 
 extern "C" {
@@ -209,24 +236,29 @@ int mgemm_moe_mxfp8_glu(const void *xq, const void *xs, const int32_t *topk_ids,
                         int64_t topk, const void *w13q, const void *w13s, const void *w2q,
                         const void *w2s, void *out, void *ws, size_t ws_bytes, void *dbg_h,
                         void *stream) {
-  if (!xq || !xs || !topk_ids || !topk_w || !w13q || !w13s || !w2q || !w2s || !out)
-    return MGEMM_ERR_INVALID_ARG;
-  if (!aligned16(xq) || !aligned16(xs) || !aligned16(topk_ids) || !aligned16(topk_w) ||
-      !aligned16(w13q) || !aligned16(w13s) || !aligned16(w2q) || !aligned16(w2s) ||
-      !aligned16(out) || (dbg_h && !aligned16(dbg_h)))
-    return MGEMM_ERR_INVALID_ARG;
-  if (T <= 0 || H <= 0 || I <= 0 || E <= 0 || topk <= 0) return MGEMM_ERR_SHAPE;
-  if (H % 64 != 0 || I % 64 != 0 || topk > 16 || E > 1024 || T > (1 << 24) ||
-      H > (1 << 20) || I > (1 << 20) || (double)T * topk * (double)(H > I ? H : I) > 4.0e18)
-    return MGEMM_ERR_SHAPE;
-  if (int rc = check_path(MGEMM_FMT_MXFP8, MGEMM_FMT_MXFP8)) return rc;
-  const size_t need = mg::moe_workspace_bytes(T, H, I, E, topk);
-  if (!ws || ws_bytes < need || !aligned16(ws)) return MGEMM_ERR_WORKSPACE;
-  mg::MoeArgs p{(const uint8_t *)xq, (const uint8_t *)xs, topk_ids, topk_w, (int)T, (int)H,
-                (int)I, (int)E, (int)topk, (const uint8_t *)w13q, (const uint8_t *)w13s,
-                (const uint8_t *)w2q, (const uint8_t *)w2s, (uint16_t *)out, ws, ws_bytes,
-                (uint8_t *)dbg_h};
-  return finish(mg::launch_moe(p, (hipStream_t)stream), "mgemm_moe_mxfp8_glu");
+  return moe_mxfp8(xq, xs, nullptr, topk_ids, topk_w, T, H, I, E, topk, w13q, w13s, w2q, w2s, out,
+                   ws, ws_bytes, dbg_h, nullptr, stream, "mgemm_moe_mxfp8_glu");
+}
+
+int mgemm_moe_mxfp8_glu_debug(const void *xq, const void *xs, const int32_t *topk_ids,
+                              const float *topk_w, int64_t T, int64_t H, int64_t I, int64_t E,
+                              int64_t topk, const void *w13q, const void *w13s, const void *w2q,
+                              const void *w2s, void *out, void *ws, size_t ws_bytes, void *dbg_h,
+                              float *dbg_gu, void *stream) {
+  return moe_mxfp8(xq, xs, nullptr, topk_ids, topk_w, T, H, I, E, topk, w13q, w13s, w2q, w2s, out,
+                   ws, ws_bytes, dbg_h, dbg_gu, stream, "mgemm_moe_mxfp8_glu_debug");
+}
+
+int mgemm_moe_mxfp8_glu_logits(const void *xq, const void *xs, const float *logits, int64_t T,
+                               int64_t H, int64_t I, int64_t E, int64_t topk, const void *w13q,
+                               const void *w13s, const void *w2q, const void *w2s, void *out,
+                               int32_t *topk_ids, float *topk_w, void *ws, size_t ws_bytes,
+                               void *dbg_h, void *stream) {
+  if (!logits) return MGEMM_ERR_INVALID_ARG;
+  if ((uintptr_t)logits & 3) return MGEMM_ERR_INVALID_ARG;
+  if (topk > E) return MGEMM_ERR_SHAPE;
+  return moe_mxfp8(xq, xs, logits, topk_ids, topk_w, T, H, I, E, topk, w13q, w13s, w2q, w2s, out,
+                   ws, ws_bytes, dbg_h, nullptr, stream, "mgemm_moe_mxfp8_glu_logits");
 }
 
 int mgemm_moe_nvfp4_glu(const void *xq, const void *xs, const float *Sx,

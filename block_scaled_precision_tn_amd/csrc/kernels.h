@@ -65,6 +65,12 @@ struct MoeArgs {
   void *ws;
   size_t ws_bytes;
   uint8_t *dbg_h;
+  // non-null: route from these FP32 router logits [T,E] (softmax, top-k) in
+  // the route-prep launch; ids / tw are then outputs it writes
+  const float *logits;
+  // optional tap: per (token, slot) row t*topk + j, the FP32 gate/up
+  // accumulators g[0..I) then u[0..I)
+  float *dbg_gu;
 };
 size_t moe_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk);
 hipError_t launch_moe(const MoeArgs &p, hipStream_t stream);

@@ -424,6 +424,11 @@ __global__ __launch_bounds__(256) void k_gateup(MoeArgs p, const int32_t *meta,
       }
       if (row < nrows) {
         const int64_t srow = r0 + row;
+        if (p.dbg_gu) {
+          float *d = p.dbg_gu + (int64_t)sorted[srow] * (2 * I);
+          d[col] = g;
+          d[I + col] = u;
+        }
         hq[srow * I + col] = (uint8_t)code;
         if (l32 == 0) hs[srow * (I / 32) + col / 32] = (uint8_t)sbyte;
         if (p.dbg_h) {
@@ -660,6 +665,14 @@ __global__ __launch_bounds__(256) void k_dec(MoeArgs p, const int32_t *meta, con
         }
         if (t < nt) {
           const int64_t srow = r0 + tb + t;
+          if (p.dbg_gu) {
+            float *d = p.dbg_gu + (int64_t)sorted[srow] * (2 * I) + c0;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              d[acc_row(r, lane)] = acc[r];
+              d[I + acc_row(r, lane)] = red[(1 * 16 + r) * 64 + lane];
+            }
+          }
           uint8_t *dq = hq + srow * I + c0;
           uint8_t *dd = p.dbg_h ? p.dbg_h + (int64_t)sorted[srow] * (I + I / 32) : nullptr;
 #pragma unroll
@@ -697,18 +710,15 @@ __global__ __launch_bounds__(256) void k_dec(MoeArgs p, const int32_t *meta, con
 }
 
 // Router top-k (softmax of the logits, the k largest, as the MoE
-// configuration routes): one wave per token, expert e in lane e % 64,
+// configuration routes) of one token by one wave: expert e in lane e % 64,
 // register e / 64.  The softmax is taken in FP32 (max, exp, a butterfly sum
 // that leaves every lane the same value, one division per weight); the k
 // experts are chosen on the logits, which orders them as the exact
-// probabilities (equal logits: the lower id first).
+// probabilities (equal logits: the lower id first).  Slot j's id and weight
+// go to ids[j], w[j] and, when given, to the LDS copies lids[j], lw[j].
 template <int PER>
-__global__ __launch_bounds__(256) void k_topk_softmax(const float *logits, int T, int E, int topk,
-                                                      int32_t *ids, float *w) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  const float *row = logits + (int64_t)t * E;
+__device__ __forceinline__ void route_token(const float *row, int E, int topk, int lane,
+                                            int32_t *ids, float *w, int32_t *lids, float *lw) {
   float v[PER], ex[PER];
   float m = -__builtin_inff();
 #pragma unroll
@@ -752,12 +762,62 @@ __global__ __launch_bounds__(256) void k_topk_softmax(const float *logits, int T
 #pragma unroll
       for (int q = 0; q < PER; ++q)
         if (q == be >> 6) {
-          ids[(int64_t)t * topk + j] = be;
-          w[(int64_t)t * topk + j] = ex[q] / s;
+          const float p = ex[q] / s;
+          ids[j] = be;
+          w[j] = p;
+          if (lids) {
+            lids[j] = be;
+            lw[j] = p;
+          }
           v[q] = -__builtin_inff();   // taken (finite logits: never chosen again)
         }
     }
   }
+}
+
+// the router alone: one wave per token
+template <int PER>
+__global__ __launch_bounds__(256) void k_topk_softmax(const float *logits, int T, int E, int topk,
+                                                      int32_t *ids, float *w) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  route_token<PER>(logits + (int64_t)t * E, E, topk, lane, ids + (int64_t)t * topk,
+                   w + (int64_t)t * topk, nullptr, nullptr);
+}
+
+// Route prep from the router logits (the four-kernel routing's k_count with
+// the router fused in): each workgroup routes RT_TOK tokens (one wave per
+// token at a time), writes their ids and weights, then counts its entries per
+// expert in LDS, reserves each expert's run of ranks with one global atomic,
+// and writes each entry's rank -- what k_topk_softmax then k_count compute,
+// without the ids' round trip through a second launch.
+constexpr int RT_TOK = 16;   // tokens per workgroup (4 waves x 4)
+template <int PER>
+__global__ __launch_bounds__(256) void k_count_logits(const float *logits, int T, int E, int topk,
+                                                      int32_t *ids, float *tw, uint32_t *counts,
+                                                      int32_t *rank) {
+  __shared__ uint32_t s_cnt[1024], s_base[1024];
+  __shared__ int32_t s_ids[RT_TOK * 16];
+  __shared__ float s_w[RT_TOK * 16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t0 = blockIdx.x * RT_TOK;
+  const int nt = T - t0 < RT_TOK ? T - t0 : RT_TOK;
+  for (int e = tid; e < E; e += 256) s_cnt[e] = 0u;
+  for (int i = wave; i < nt; i += 4) {
+    const int64_t t = t0 + i;
+    route_token<PER>(logits + t * E, E, topk, lane, ids + t * topk, tw + t * topk,
+                     s_ids + i * topk, s_w + i * topk);
+  }
+  __syncthreads();
+  const int n = nt * topk;            // entries of this workgroup (at most 256)
+  const int e = tid < n ? s_ids[tid] : -1;
+  const uint32_t lr = tid < n ? atomicAdd(&s_cnt[e], 1u) : 0u;
+  __syncthreads();
+  for (int x = tid; x < E; x += 256)
+    if (s_cnt[x] != 0u) s_base[x] = atomicAdd(&counts[x], s_cnt[x]);
+  __syncthreads();
+  if (tid < n) rank[(int64_t)t0 * topk + tid] = (int32_t)(s_base[e] + lr);
 }
 
 // one thread per (token, 4 columns): slots summed in order 0..topk-1; every
@@ -784,18 +844,31 @@ __global__ void k_combine(const float *y, const int32_t *pos, int T, int H, int 
 
 // Decode-sized routing (R <= 1024 entries, E <= 1024 experts) in one
 // workgroup: what k_prep, k_count, k_scan and k_scatter do, with the expert
-// counters and both scans in LDS, so the call spends one launch on it.
+// counters and both scans in LDS, so the call spends one launch on it.  With
+// LOGITS the router runs first in the same workgroup (one wave per token, as
+// k_topk_softmax): it writes the T tokens' ids and weights to `ids` / `tw`
+// (outputs then) and keeps them in LDS for the counting.
+template <bool LOGITS, int PER>
 __global__ __launch_bounds__(1024) void k_route_small(const int32_t *ids, const float *tw, int R,
                                                       int E, int32_t *offs, int32_t *meta,
                                                       int32_t *tile_e, int32_t *tile_r,
                                                       int32_t *tile_n, int32_t *pos,
-                                                      int32_t *sorted, float *wsorted) {
+                                                      int32_t *sorted, float *wsorted,
+                                                      const float *logits, int T, int topk) {
   __shared__ uint32_t s_cnt[1024];
   __shared__ int s_rows[1024], s_tiles[1024];
+  __shared__ int32_t s_ids[LOGITS ? 1024 : 1];
+  __shared__ float s_w[LOGITS ? 1024 : 1];
   const int tid = threadIdx.x;
   s_cnt[tid] = 0u;
+  if constexpr (LOGITS) {
+    const int lane = tid & 63;
+    for (int t = tid >> 6; t < T; t += 16)
+      route_token<PER>(logits + (int64_t)t * E, E, topk, lane, (int32_t *)ids + t * topk,
+                       (float *)tw + t * topk, s_ids + t * topk, s_w + t * topk);
+  }
   __syncthreads();
-  const int e = tid < R ? ids[tid] : -1;
+  const int e = tid < R ? (LOGITS ? s_ids[tid] : ids[tid]) : -1;
   const bool ok = e >= 0 && e < E;
   const uint32_t rk = ok ? atomicAdd(&s_cnt[e], 1u) : 0u;   // rank within the expert
   __syncthreads();
@@ -826,7 +899,7 @@ __global__ __launch_bounds__(1024) void k_route_small(const int32_t *ids, const 
       const int p = s_rows[e] - (int)s_cnt[e] + (int)rk;
       pos[tid] = p;
       sorted[p] = tid;
-      wsorted[p] = tw[tid];
+      wsorted[p] = LOGITS ? s_w[tid] : tw[tid];
     } else {
       pos[tid] = -1;
     }
@@ -866,8 +939,22 @@ hipError_t launch_moe(const MoeArgs &p, hipStream_t stream) {
   if (dec_path(p)) {
     // decode-sized: one routing launch; every active tile has at least one
     // row, so at most R tiles
-    hipLaunchKernelGGL(k_route_small, dim3(1), dim3(1024), 0, stream, p.ids, p.tw, L.R, p.E, offs,
-                       meta, tile_e, tile_r, tile_n, pos, sorted, wsorted);
+    if (!p.logits)
+      hipLaunchKernelGGL((k_route_small<false, 1>), dim3(1), dim3(1024), 0, stream, p.ids, p.tw, L.R,
+                         p.E, offs, meta, tile_e, tile_r, tile_n, pos, sorted, wsorted, nullptr, p.T,
+                         p.topk);
+    else if (p.E <= 64)
+      hipLaunchKernelGGL((k_route_small<true, 1>), dim3(1), dim3(1024), 0, stream, p.ids, p.tw, L.R,
+                         p.E, offs, meta, tile_e, tile_r, tile_n, pos, sorted, wsorted, p.logits,
+                         p.T, p.topk);
+    else if (p.E <= 256)
+      hipLaunchKernelGGL((k_route_small<true, 4>), dim3(1), dim3(1024), 0, stream, p.ids, p.tw, L.R,
+                         p.E, offs, meta, tile_e, tile_r, tile_n, pos, sorted, wsorted, p.logits,
+                         p.T, p.topk);
+    else
+      hipLaunchKernelGGL((k_route_small<true, 16>), dim3(1), dim3(1024), 0, stream, p.ids, p.tw,
+                         L.R, p.E, offs, meta, tile_e, tile_r, tile_n, pos, sorted, wsorted,
+                         p.logits, p.T, p.topk);
     const unsigned ty = (unsigned)(L.maxtiles < L.R ? L.maxtiles : L.R);
     const dim3 gg(p.I / 32, ty), gd(p.H / DROWS, ty);
     // at most two active workgroups per CU (of 256): the deeper ring
@@ -890,8 +977,24 @@ hipError_t launch_moe(const MoeArgs &p, hipStream_t stream) {
   }
   const int rb = (L.R + 255) / 256;
   hipLaunchKernelGGL(k_prep, dim3((p.E + 255) / 256), dim3(256), 0, stream, counts, p.E);
-  hipLaunchKernelGGL(k_count, dim3((L.R + 1023) / 1024), dim3(1024), 0, stream, p.ids, L.R, p.E,
-                     counts, pos);
+  if (!p.logits) {
+    hipLaunchKernelGGL(k_count, dim3((L.R + 1023) / 1024), dim3(1024), 0, stream, p.ids, L.R, p.E,
+                       counts, pos);
+  } else {
+    // the router fused into the count: ids and weights written here
+    const dim3 gr((unsigned)((p.T + RT_TOK - 1) / RT_TOK));
+    int32_t *ids = (int32_t *)p.ids;
+    float *tw = (float *)p.tw;
+    if (p.E <= 64)
+      hipLaunchKernelGGL(k_count_logits<1>, gr, dim3(256), 0, stream, p.logits, p.T, p.E, p.topk,
+                         ids, tw, counts, pos);
+    else if (p.E <= 256)
+      hipLaunchKernelGGL(k_count_logits<4>, gr, dim3(256), 0, stream, p.logits, p.T, p.E, p.topk,
+                         ids, tw, counts, pos);
+    else
+      hipLaunchKernelGGL(k_count_logits<16>, gr, dim3(256), 0, stream, p.logits, p.T, p.E, p.topk,
+                         ids, tw, counts, pos);
+  }
   hipLaunchKernelGGL(k_scan, dim3(1), dim3(256), 0, stream, counts, p.E, offs, meta, tile_e,
                      tile_r, tile_n);
   hipLaunchKernelGGL(k_scatter, dim3(rb), dim3(256), 0, stream, p.ids, p.tw, L.R, offs, pos, sorted,
@@ -942,8 +1045,9 @@ hipError_t launch_moe4(const Moe4Args &p, hipStream_t stream) {
   float *y = (float *)(w + L.y);
   const int64_t TH4 = (int64_t)p.T * (p.H / 4);
   if (L.R <= 1024) {
-    hipLaunchKernelGGL(k_route_small, dim3(1), dim3(1024), 0, stream, p.ids, p.tw, L.R, p.E, offs,
-                       meta, tile_e, tile_r, tile_n, pos, sorted, wsorted);
+    hipLaunchKernelGGL((k_route_small<false, 1>), dim3(1), dim3(1024), 0, stream, p.ids, p.tw, L.R,
+                       p.E, offs, meta, tile_e, tile_r, tile_n, pos, sorted, wsorted, nullptr, p.T,
+                       p.topk);
   } else {
     const int rb = (L.R + 255) / 256;
     hipLaunchKernelGGL(k_prep, dim3((p.E + 255) / 256), dim3(256), 0, stream, counts, p.E);

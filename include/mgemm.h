@@ -191,6 +191,34 @@ int mgemm_moe_mxfp8_glu(const void *xq, const void *xs, const int32_t *topk_ids,
                         const void *w2q, const void *w2s, void *out, void *ws,
                         size_t ws_bytes, void *dbg_h, void *stream);
 
+/* mgemm_moe_mxfp8_glu with a second debug tap for stage-wise checks of the
+   path: dbg_gu, NULL or a device buffer of T*topk*2*I floats (16-byte
+   aligned), receives each (token, slot) row's FP32 gate/up accumulators
+   g[0..I) then u[0..I) (before the GLU) at row t*topk + j; rows of dropped
+   slots are not written.  Everything else as mgemm_moe_mxfp8_glu. */
+int mgemm_moe_mxfp8_glu_debug(const void *xq, const void *xs, const int32_t *topk_ids,
+                              const float *topk_w, int64_t T, int64_t H, int64_t I, int64_t E,
+                              int64_t topk, const void *w13q, const void *w13s, const void *w2q,
+                              const void *w2s, void *out, void *ws, size_t ws_bytes, void *dbg_h,
+                              float *dbg_gu, void *stream);
+
+/* The MXFP8 grouped MoE GLU above routed from the router's FP32 logits
+   [T,E] in the same call: the top-k routing from the softmax of the logits
+   (as mgemm_moe_route_topk computes it, bit for bit: p = softmax in FP32,
+   the topk experts of largest p in descending order, equal logits to the
+   lower id, weights p not renormalised) runs inside the route-prep launch
+   that counts each expert's rows and ranks them, so the ids never make a
+   round trip between two launches.  topk_ids [T,topk] int32 and topk_w
+   [T,topk] FP32 are OUTPUTS (device buffers, 16-byte aligned) that receive
+   the routing; the result equals mgemm_moe_mxfp8_glu called on them.
+   logits: finite FP32, 4-byte aligned; topk <= E.  Other arguments,
+   workspace, limits and errors as mgemm_moe_mxfp8_glu. */
+int mgemm_moe_mxfp8_glu_logits(const void *xq, const void *xs, const float *logits, int64_t T,
+                               int64_t H, int64_t I, int64_t E, int64_t topk, const void *w13q,
+                               const void *w13s, const void *w2q, const void *w2s, void *out,
+                               int32_t *topk_ids, float *topk_w, void *ws, size_t ws_bytes,
+                               void *dbg_h, void *stream);
+
 /* NVFP4 grouped mixture-of-experts GLU: the GLU MoE above (same FlashInfer
    skill page, which lists an NVFP4 MoE, moe_nvfp4_swapab, beside the MXFP8
    one) with every operand in NVFP4, computed on the exact FP8 route of the

@@ -61,6 +61,9 @@ def _load():
     lib.orc_fp8route_w4a4_rows.argtypes = [C.c_void_p] * 4 + [i64, i64, C.c_void_p]
     lib.orc_fp8route_w4a8_rows.restype = None
     lib.orc_fp8route_w4a8_rows.argtypes = [C.c_void_p] * 3 + [i64, i64, C.c_void_p]
+    lib.orc_fp8route_w4a4_points.restype = C.c_int
+    lib.orc_fp8route_w4a4_points.argtypes = [C.c_void_p] * 4 + [i64] * 3 + [C.c_void_p] * 2 + \
+        [i64, C.c_void_p, C.c_int]
     lib.orc_enc_e4m3_rne_sat.restype = C.c_uint8
     lib.orc_enc_e4m3_rne_sat.argtypes = [f64]
     lib.orc_mxq.restype = None
@@ -230,6 +233,22 @@ def fp8route_w4a4_rows(aq, as_, wq, ws) -> np.ndarray:
     out = np.zeros(aq.shape[0], np.float32)
     _load().orc_fp8route_w4a4_rows(aq.ctypes.data, as_.ctypes.data, wq.ctypes.data,
                                    ws.ctypes.data, aq.shape[1] * 2, aq.shape[0], out.ctypes.data)
+    return out
+
+
+def fp8route_w4a4_points(aq, as_, wq, ws, m, n, nthreads=None) -> np.ndarray:
+    """Emulated exact-FP8 route (FP32, before the tensor scales) at the points
+    (m[i], n[i]): row m[i] of A against row n[i] of W."""
+    aq, as_, wq, ws = (np.ascontiguousarray(x, dtype=np.uint8) for x in (aq, as_, wq, ws))
+    m = np.ascontiguousarray(m, dtype=np.int64).ravel()
+    n = np.ascontiguousarray(n, dtype=np.int64).ravel()
+    out = np.zeros(m.size, np.float32)
+    rc = _load().orc_fp8route_w4a4_points(aq.ctypes.data, as_.ctypes.data, wq.ctypes.data,
+                                          ws.ctypes.data, aq.shape[0], wq.shape[0],
+                                          aq.shape[1] * 2, m.ctypes.data, n.ctypes.data, m.size,
+                                          out.ctypes.data, _nthreads(nthreads))
+    if rc != 0:
+        raise ValueError("oracle: bad fp8route points arguments")
     return out
 
 

@@ -249,6 +249,34 @@ void orc_fp8route_w4a8_rows(const uint8_t *a8, const uint8_t *wq,
     out[i] = orc_fp8route_w4a8_point(a8 + i * K, wq + i * (K / 2), ws + i * (K / 16), K);
 }
 
+typedef struct {
+  const uint8_t *aq, *as, *wq, *ws;
+  int64_t K;
+  const int64_t *m, *n;
+  float *out;
+} orc_route_ctx;
+
+static void orc_route_points_range(void *p, int64_t lo, int64_t hi) {
+  orc_route_ctx *c = (orc_route_ctx *)p;
+  const int64_t K = c->K;
+  for (int64_t i = lo; i < hi; i++)
+    c->out[i] = orc_fp8route_w4a4_point(c->aq + c->m[i] * (K / 2), c->as + c->m[i] * (K / 16),
+                                        c->wq + c->n[i] * (K / 2), c->ws + c->n[i] * (K / 16), K);
+}
+
+int orc_fp8route_w4a4_points(const uint8_t *aq, const uint8_t *as, const uint8_t *wq,
+                             const uint8_t *ws, int64_t M, int64_t N, int64_t K,
+                             const int64_t *m, const int64_t *n, int64_t npts, float *out,
+                             int nthreads) {
+  if (!aq || !as || !wq || !ws || K <= 0 || K % 16 || npts < 0) return -1;
+  if (npts > 0 && (!m || !n || !out)) return -1;
+  for (int64_t i = 0; i < npts; i++)
+    if (m[i] < 0 || m[i] >= M || n[i] < 0 || n[i] >= N) return -1;
+  orc_route_ctx c = {aq, as, wq, ws, K, m, n, out};
+  orc_parallel(npts, nthreads, &c, orc_route_points_range);
+  return 0;
+}
+
 /* --------------------------------------------------------------- encoders */
 
 uint8_t orc_enc_e4m3_rne_sat(double v) {

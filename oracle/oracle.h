@@ -83,6 +83,13 @@ void orc_fp8route_w4a4_rows(const uint8_t *aq, const uint8_t *as,
 void orc_fp8route_w4a8_rows(const uint8_t *a8, const uint8_t *wq,
                             const uint8_t *ws, int64_t K, int64_t nrows, float *out);
 
+/* the emulated route at points: row m[i] of A ([M,K/2] codes, [M,K/16]
+   scales) against row n[i] of W; returns 0, or -1 on bad arguments */
+int orc_fp8route_w4a4_points(const uint8_t *aq, const uint8_t *as, const uint8_t *wq,
+                             const uint8_t *ws, int64_t M, int64_t N, int64_t K,
+                             const int64_t *m, const int64_t *n, int64_t npts, float *out,
+                             int nthreads);
+
 /* --- encoders used by the MoE requant step (and pinned by round trips) --- */
 /* round-to-nearest-even onto the E4M3-FN grid, saturating at +-448 */
 uint8_t orc_enc_e4m3_rne_sat(double v);

@@ -67,11 +67,12 @@ def test_w4a8_decode_full_size(Md):
 
 
 def test_moe_full_size_sampled_tokens():
-    from test_gpu_moe import _check_down_combine, _check_requant, run_moe
+    from test_gpu_moe import _check_down_combine, _check_gateup, _check_requant, run_moe
     T, H, I, E, topk = 4096, 4096, 1536, 64, 8
     inp = synth.moe(T, H, I, E, topk, seed=0)
-    out, d = run_moe(inp, T, H, I, E, topk)
+    out, d, gu = run_moe(inp, T, H, I, E, topk, gu=True)
     tokens = np.array([0, 1, 777, 2048, 4095])
+    _check_gateup(inp, gu, T, H, I, topk, tokens=tokens)
     nd = _check_requant(inp, d, T, H, I, topk, tokens=tokens)
     assert nd <= max(4, len(tokens) * topk * I // 100), nd
     _check_down_combine(inp, d, out, T, H, I, topk, tokens)
@@ -80,11 +81,12 @@ def test_moe_full_size_sampled_tokens():
 @pytest.mark.parametrize("T", [1, 16])
 def test_moe_decode_full_size(T):
     """Decode-sized token counts at the full MoE shape (the swap-AB kernels)."""
-    from test_gpu_moe import _check_down_combine, _check_requant, run_moe
+    from test_gpu_moe import _check_down_combine, _check_gateup, _check_requant, run_moe
     H, I, E, topk = 4096, 1536, 64, 8
     inp = synth.moe(T, H, I, E, topk, seed=T)
-    out, d = run_moe(inp, T, H, I, E, topk)
+    out, d, gu = run_moe(inp, T, H, I, E, topk, gu=True)
     tokens = np.arange(T) if T <= 4 else np.array([0, 5, T - 1])
+    _check_gateup(inp, gu, T, H, I, topk, tokens=tokens)
     nd = _check_requant(inp, d, T, H, I, topk, tokens=tokens)
     assert nd <= max(4, len(tokens) * topk * I // 100), nd
     _check_down_combine(inp, d, out, T, H, I, topk, tokens)

@@ -60,7 +60,7 @@ def _check(kind, dy, b, m=None, n=None, what=""):
     if m is not None:
         g32, g16 = g32[m, n], g16[m, n]
     check_f32(g32, c64, b64, what=what + " fp32")
-    check_bf16_vs(g16, c64, b64, what=what + " bf16")
+    check_bf16_vs(g16, c64, b64, what=what + " bf16", g32=g32)
 
 
 # ragged tiles in every dimension; K (and N for wgrad) multiples of 8, the

@@ -34,18 +34,42 @@ def _gpu():
     yield
 
 
-def run_moe(inp, T, H, I, E, topk, dbg=True):
+def run_moe(inp, T, H, I, E, topk, dbg=True, gu=False):
+    """Output bits [T,H], the re-quantised h rows (dbg) and, with gu, the FP32
+    gate/up accumulator rows [T*topk, 2I] as well."""
     import block_scaled_precision_tn_amd as mg
     from gpu_cases import dev
     out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
     dbg_h = torch.zeros(T * topk * (I + I // 32), dtype=torch.uint8, device="cuda") if dbg else None
+    dbg_gu = torch.zeros(T * topk * 2 * I, dtype=torch.float32, device="cuda") if gu else None
     mg.mgemm_moe_mxfp8_glu(dev(inp["xq"]), dev(inp["xs"]), dev(inp["ids"]), dev(inp["tw"]),
                            dev(inp["w13q"]), dev(inp["w13s"]), dev(inp["w2q"]), dev(inp["w2s"]),
-                           out, dbg_h=dbg_h)
+                           out, dbg_h=dbg_h, dbg_gu=dbg_gu)
     torch.cuda.synchronize()
     o = out.view(torch.int16).cpu().numpy().view(np.uint16)
     d = dbg_h.cpu().numpy().reshape(T * topk, I + I // 32) if dbg else None
+    if gu:
+        return o, d, dbg_gu.cpu().numpy().reshape(T * topk, 2 * I)
     return o, d
+
+
+def _check_gateup(inp, gu, T, H, I, topk, tokens=None):
+    """Stage (i): the kernel's FP32 gate/up accumulators against the oracle's
+    g and u, within 1e-5 * sum|x w| plus the MX MFMA's summation-window
+    allowance.  Returns the largest err / (1e-5 B)."""
+    from checks import check_f32
+    worst = 0.0
+    for t in (range(T) if tokens is None else tokens):
+        for j in range(topk):
+            e = int(inp["ids"][t, j])
+            if not 0 <= e < inp["w13q"].shape[0]:
+                continue
+            g, u, bg, bu = oracle.moe_gateup(inp["xq"], inp["xs"], t, e, inp["w13q"], inp["w13s"], H, I)
+            hw = mx_window(inp["xq"][t][None, :], inp["xs"][t][None, :], inp["w13q"][e], inp["w13s"][e])
+            row = gu[t * topk + j]
+            worst = max(worst, check_f32(row, np.r_[g, u], np.r_[bg, bu], what=f"gate/up {t},{j}",
+                                         extra=hw))
+    return worst
 
 
 def test_moe_hand_case():
@@ -90,6 +114,8 @@ def _check_requant(inp, d, T, H, I, topk, tol=1e-5, tokens=None):
     for t in (range(T) if tokens is None else tokens):
         for j in range(topk):
             e = int(inp["ids"][t, j])
+            if not 0 <= e < inp["w13q"].shape[0]:
+                continue                         # a dropped slot
             g, u, bg, bu = oracle.moe_gateup(inp["xq"], inp["xs"], t, e, inp["w13q"], inp["w13s"], H, I)
             hq, hs = oracle.moe_glu_requant(g, u)
             gq, gs = d[t * topk + j, :I], d[t * topk + j, I:]
@@ -98,9 +124,8 @@ def _check_requant(inp, d, T, H, I, topk, tol=1e-5, tokens=None):
             s = expit(g)
             dsilu = s * (1 + g * (1 - s))
             h = g * s * u
-            xg = _mx_vals(inp["xq"][t], inp["xs"][t])
-            w13 = _mx_vals(inp["w13q"][e], inp["w13s"][e])
-            hw = fp8_window_bound(xg[None, :] * w13)
+            hw = mx_window(inp["xq"][t][None, :], inp["xs"][t][None, :], inp["w13q"][e],
+                           inp["w13s"][e])
             eg = tol * bg + hw[:I]
             eu = tol * bu + hw[I:]
             dh = np.abs(dsilu * u) * eg + np.abs(g * s) * eu + 4 * 2.0 ** -24 * np.abs(h)
@@ -123,11 +148,15 @@ def _check_requant(inp, d, T, H, I, topk, tol=1e-5, tokens=None):
     return n_diff
 
 
-def _mx_vals(q, s):
-    """decoded MXFP8 values (torch's E4M3 / E8M0 decoders), [..., K]"""
-    v = _e4m3_val(q)
-    sc = torch.tensor(np.asarray(s, np.uint8)).view(torch.float8_e8m0fnu).double().numpy()
-    return v * np.repeat(sc, 32, axis=-1)
+def mx_window(qa, sa, qw, sw):
+    """FP8 MFMA summation-window allowance (fp8_window_bound) of MXFP8 dot
+    products: the MX MFMA multiplies the E4M3 codes, and a group of 8's sum is
+    then scaled by the two E8M0 block scales of its 32-element block.
+    qa/sa: codes [.., K] and scales [.., K/32] of one side, qw/sw the other's
+    (broadcastable); returns the allowance per leading index."""
+    e8 = lambda s: torch.tensor(np.asarray(s, np.uint8)).view(torch.float8_e8m0fnu).double().numpy()  # noqa: E731
+    g = np.repeat(e8(sa) * e8(sw), 4, axis=-1)
+    return fp8_window_bound(_e4m3_val(qa), _e4m3_val(qw), g)
 
 
 def _check_down_combine(inp, d, out, T, H, I, topk, tokens):
@@ -141,13 +170,15 @@ def _check_down_combine(inp, d, out, T, H, I, topk, tokens):
     for ti, t in enumerate(tokens):
         for j in range(topk):
             e = int(inp["ids"][t, j])
+            if not 0 <= e < inp["w13q"].shape[0]:
+                continue                         # a dropped slot
             row = d[t * topk + j]
             y, by = oracle.moe_down(row[:I].copy(), row[I:].copy(), e, inp["w2q"], inp["w2s"], H, I)
             w = float(inp["tw"][t, j])
             ref[ti] += w * y
             bnd[ti] += abs(w) * by
-            hv = _mx_vals(row[:I], row[I:])
-            extra[ti] += abs(w) * fp8_window_bound(hv[None, :] * _mx_vals(inp["w2q"][e], inp["w2s"][e]))
+            extra[ti] += abs(w) * mx_window(row[:I][None, :], row[I:][None, :], inp["w2q"][e],
+                                            inp["w2s"][e])
         extra[ti] += topk * 2.0 ** -23 * bnd[ti]
     check_bf16_vs(out[tokens], ref, bnd, what="moe out", extra=extra)
 
@@ -163,7 +194,9 @@ def _check_down_combine(inp, d, out, T, H, I, topk, tokens):
                                           (16, 128, 128, 64, 8), (5, 64, 128, 4, 2)])
 def test_moe_stagewise(T, H, I, E, topk):
     inp = synth.moe(T, H, I, E, topk, seed=T + E)
-    out, d = run_moe(inp, T, H, I, E, topk)
+    out, d, gu = run_moe(inp, T, H, I, E, topk, gu=True)
+    worst = _check_gateup(inp, gu, T, H, I, topk)
+    print(f"[parity] moe {T}x{H}x{I} E={E} top{topk}: gate/up max err/B {worst:.3g}")
     nb = _check_requant(inp, d, T, H, I, topk)
     assert nb <= max(4, T * topk * I // 100), nb   # differing codes are rare
     _check_down_combine(inp, d, out, T, H, I, topk, np.arange(T))
@@ -236,3 +269,21 @@ def test_moe_repeat_bit_identical():
     o2, d2 = run_moe(inp, T, H, I, E, topk)
     assert np.array_equal(d1, d2)
     assert np.array_equal(o1, o2)
+
+
+@pytest.mark.parametrize("T", [5, 40])   # one-workgroup routing (decode kernels), four-kernel routing
+def test_moe_out_of_range_ids_dropped(T):
+    """Expert ids outside [0, E) (-1 and E here) are dropped: the output is
+    the combine of the remaining slots, and a dropped slot's debug row is
+    never written."""
+    H, I, E, topk = 256, 128, 8, 4
+    inp = synth.moe(T, H, I, E, topk, seed=13 + T)
+    ids = inp["ids"].copy()
+    ids[::2, 1] = -1
+    ids[1::3, 3] = E
+    inp["ids"] = ids
+    out, d = run_moe(inp, T, H, I, E, topk)
+    bad = (ids < 0) | (ids >= E)
+    assert bad.any() and np.all(d[bad.ravel()] == 0)
+    _check_requant(inp, d, T, H, I, topk)
+    _check_down_combine(inp, d, out, T, H, I, topk, np.arange(T))

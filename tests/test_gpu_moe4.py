@@ -66,6 +66,8 @@ def _check_requant(inp, d, T, H, I, topk, tokens, tol=1e-5):
     for t in tokens:
         for j in range(topk):
             e = int(inp["ids"][t, j])
+            if not 0 <= e < inp["w13q"].shape[0]:
+                continue                         # a dropped slot
             g, u, bg, bu = oracle.moe4_gateup(inp, t, e, H, I)
             hq, hs = oracle.moe4_glu_requant(g, u, Sh)
             gq, gs = d[t * topk + j, :I // 2], d[t * topk + j, I // 2:]
@@ -112,6 +114,8 @@ def _check_down_combine(inp, d, out, T, H, I, topk, tokens):
     for ti, t in enumerate(tokens):
         for j in range(topk):
             e = int(inp["ids"][t, j])
+            if not 0 <= e < inp["w13q"].shape[0]:
+                continue                         # a dropped slot
             row = d[t * topk + j]
             y, by = oracle.moe4_down(row[:I // 2].copy(), row[I // 2:].copy(), Sh, e, inp, H, I)
             w = float(inp["tw"][t, j])
@@ -184,4 +188,23 @@ def test_moe4_full_size_sampled_tokens():
     tokens = np.array([0, 1, 2048, 4095])
     nd = _check_requant(inp, d, T, H, I, topk, tokens)
     assert nd <= max(4, len(tokens) * topk * I // 100), nd
+    _check_down_combine(inp, d, out, T, H, I, topk, tokens)
+
+
+@pytest.mark.parametrize("T", [5, 300])   # one-launch routing (T * topk <= 1024), four-kernel routing
+def test_moe4_out_of_range_ids_dropped(T):
+    """Expert ids outside [0, E) (-1 and E here) are dropped: the output is
+    the combine of the remaining slots, and a dropped slot's debug row is
+    never written."""
+    H, I, E, topk = 128, 128, 8, 4
+    inp = synth.moe_nvfp4(T, H, I, E, topk, seed=17 + T)
+    ids = inp["ids"].copy()
+    ids[::2, 1] = -1
+    ids[1::3, 3] = E
+    inp["ids"] = ids
+    out, d = run_moe4(inp, T, H, I, E, topk)
+    bad = (ids < 0) | (ids >= E)
+    assert bad.any() and np.all(d[bad.ravel()] == 0)
+    tokens = np.arange(T) if T <= 64 else np.arange(0, T, 7)
+    _check_requant(inp, d, T, H, I, topk, tokens)
     _check_down_combine(inp, d, out, T, H, I, topk, tokens)

@@ -256,3 +256,30 @@ def test_plan_on_device():
                                    A.data_ptr(), 32, 32, 33, 0, None)
         mg._check("mgemm_w4a16", rc)
     assert ei.value.status == -2
+
+
+def test_w4a8_concurrent_streams_own_workspaces():
+    """Calls on two streams get two cached workspaces (their split-K partials
+    never mix) and both results match the oracle."""
+    import block_scaled_precision_tn_amd as mg
+    from gpu_cases import check_f32, dev, oracle_full, scalar
+    cur = torch.cuda.current_stream()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    runs = []
+    for s, seed in ((s1, 61), (s2, 62)):
+        inp = synth.w4a8(16, 384, 2048, seed=seed)
+        args = (dev(inp["aq"]), dev(inp["atok"]), dev(inp["wq"]), dev(inp["ws"]), scalar(inp["Sw"]))
+        runs.append((s, inp, args, torch.empty((16, 384), dtype=torch.float32, device="cuda")))
+    for s, _, _, _ in runs:
+        s.wait_stream(cur)                      # inputs were copied on the current stream
+    for _ in range(3):
+        for s, _, args, C in runs:
+            mg.mgemm_w4a8(*args, C, stream=s)
+    torch.cuda.synchronize()
+    w1 = mg.workspace(1, "w4a8", s1)
+    w2 = mg.workspace(1, "w4a8", s2)
+    assert w1.data_ptr() != w2.data_ptr()
+    for _, inp, _, C in runs:
+        c64, b64 = oracle_full("w4a8", inp)
+        from gpu_cases import w4a8_window
+        check_f32(C.cpu().numpy(), c64, b64, what="w4a8 stream", extra=w4a8_window(inp))

@@ -319,6 +319,55 @@ def test_mxq_matches_independent_quantiser():
     assert normal.sum() > 1000
 
 
+def test_mxq_hand_cases():
+    """The MX exponent rule and element rounding against hand derivations from
+    the OCP MX conversion rule (tests/golden/mx_quant_hand.json), including a
+    block whose code changes if the exponent offset is 7 instead of 8, ties
+    to the even mantissa, saturation, the all-zero block and small values."""
+    g = json.load(open(os.path.join(GOLD, "mx_quant_hand.json")))
+    for blk in g["blocks"]:
+        v = np.zeros(32, np.float32)
+        for k, x in blk["values"].items():
+            v[int(k)] = x
+        codes, scales = oracle.mxq(v)
+        want = np.zeros(32, np.uint8)
+        for k, c in blk["codes"].items():
+            want[int(k)] = int(c, 16)
+        assert scales[0] == blk["scale"], blk["derivation"]
+        assert np.array_equal(codes, want), (codes, blk["derivation"])
+
+
+def _moe_hand_inputs(g):
+    H, I = g["H"], g["I"]
+    return dict(
+        xq=np.full((1, H), int(g["x_code"], 16), np.uint8),
+        xs=np.full((1, H // 32), g["x_scale"], np.uint8),
+        w13q=np.concatenate([np.full((1, I, H), int(g["gate_code"], 16), np.uint8),
+                             np.full((1, I, H), int(g["up_code"], 16), np.uint8)], axis=1),
+        w13s=np.full((1, 2 * I, H // 32), g["w13_scale"], np.uint8),
+        w2q=np.full((1, H, I), int(g["w2_code"], 16), np.uint8),
+        w2s=np.full((1, H, I // 32), g["w2_scale"], np.uint8),
+        ids=np.zeros((1, 1), np.int32), tw=np.ones((1, 1), np.float32))
+
+
+@pytest.mark.parametrize("name", ["moe_hand.json", "moe_hand_128.json"])
+def test_moe_hand_cases(name):
+    """Hand-computed one-token MXFP8 MoE cases: every stage of the oracle
+    (gate/up, GLU, MX re-quantisation, down, combine, BF16) against the
+    derivation in the golden file."""
+    g = json.load(open(os.path.join(GOLD, name)))
+    H, I = g["H"], g["I"]
+    inp = _moe_hand_inputs(g)
+    gg, u, _, _ = oracle.moe_gateup(inp["xq"], inp["xs"], 0, 0, inp["w13q"], inp["w13s"], H, I)
+    hq, hs = oracle.moe_glu_requant(gg, u)
+    assert np.all(hq == int(g["h_code"], 16)) and np.all(hs == g["h_scale"]), (hq[:4], hs)
+    y, _ = oracle.moe_down(hq, hs, 0, inp["w2q"], inp["w2s"], H, I)
+    assert np.all(y == g["out"])
+    o64, _ = oracle.moe_tokens(inp, 1, H, I, 1, 1, [0])
+    assert np.all(o64 == g["out"])
+    assert oracle.bf16_rne(np.array([g["out"]]))[0] == int(g["out_bf16"], 16)
+
+
 # --------------------------------------------------------------------- MoE
 def _tiny_moe(seed=9, T=6, H=64, I=64, E=3, topk=2):
     inp = synth.moe(T, H, I, E, topk, seed=seed, w_std=0.2)
