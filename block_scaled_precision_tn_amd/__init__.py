@@ -70,6 +70,7 @@ def load() -> C.CDLL:
         "mgemm_bf16": (i32, [vp, vp, vp, i64, i64, i64, i32, vp]),
         "mgemm_w4a16": (i32, [vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]),
         "mgemm_w4a8": (i32, [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, C.c_size_t, vp]),
+        "mgemm_w4a8_noalloc": (i32, [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]),
         "mgemm_w4a4": (i32, [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]),
         "mgemm_moe_mxfp8_glu": (i32, [vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, vp, vp, vp,
                                       vp, vp, C.c_size_t, vp, vp]),
@@ -237,6 +238,27 @@ def mgemm_w4a8(Aq, a_tok, Wq, Ws, Sw, C_out, ws: Optional[torch.Tensor] = None, 
     _check("mgemm_w4a8", load().mgemm_w4a8(Aq.data_ptr(), a_tok.data_ptr(), Wq.data_ptr(),
                                            Ws.data_ptr(), Sw.data_ptr(), C_out.data_ptr(), M, N, K,
                                            _out_f32(C_out), wp, wb, _stream(stream)))
+    return C_out
+
+
+W4A8_NOALLOC_MAX_WS = 48 << 20   # MGEMM_W4A8_NOALLOC_MAX_WS
+
+
+def mgemm_w4a8_noalloc(Aq, a_tok, Wq, Ws, Sw, C_out, stream=None):
+    """mgemm_w4a8 with the split-K partials in the library's fixed per-device
+    buffer: allocates nothing (for graph capture and allocation-free loops).
+    Calls that overlap on one GPU share that buffer and must be ordered."""
+    M, K = Aq.shape
+    N = Wq.shape[0]
+    _need(Aq, "Aq", _U8, (M, K))
+    _need(a_tok, "a_tok", _F32, numel=M)
+    _need(Wq, "Wq", _U8, (N, K // 2))
+    _need(Ws, "Ws", _U8, (N, K // 16))
+    _need(Sw, "Sw", _F32, numel=1)
+    _need(C_out, "C", _C_T, (M, N))
+    _check("mgemm_w4a8_noalloc", load().mgemm_w4a8_noalloc(
+        Aq.data_ptr(), a_tok.data_ptr(), Wq.data_ptr(), Ws.data_ptr(), Sw.data_ptr(),
+        C_out.data_ptr(), M, N, K, _out_f32(C_out), _stream(stream)))
     return C_out
 
 

@@ -154,6 +154,25 @@ int mgemm_w4a8(const void *Aq, const float *a_tok, const void *Wq, const void *W
                const float *Sw, void *C, int64_t M, int64_t N, int64_t K, int out_f32,
                void *ws, size_t ws_bytes, void *stream);
 
+/* W4A8 without a workspace argument, for callers that cannot allocate
+   (code under HIP graph capture, tight serving loops, harnesses that forbid
+   hipMalloc).  Computes exactly what mgemm_w4a8 computes, with the same
+   kernels and results, but keeps the split-K partials in a fixed device
+   buffer of MGEMM_W4A8_NOALLOC_MAX_WS bytes that the library holds on every
+   device it runs on, until the process ends.  The call allocates no memory
+   (no hipMalloc, hipFree or allocating library routine); its first call on a
+   device looks up that device's buffer address.  A call whose
+   mgemm_workspace_bytes(MGEMM_OP_W4A8, M, N, K, ...) exceeds the buffer
+   returns MGEMM_ERR_WORKSPACE before enqueuing anything (N = 5376, K = 14336
+   fits up to M = 128).  The buffer needs no particular contents, but every
+   call on one device shares it: calls that overlap on one GPU (on different
+   streams, or from several host threads) race and must be ordered by the
+   caller.  Other arguments and errors as mgemm_w4a8. */
+#define MGEMM_W4A8_NOALLOC_MAX_WS ((size_t)48 << 20)
+int mgemm_w4a8_noalloc(const void *Aq, const float *a_tok, const void *Wq, const void *Ws,
+                       const float *Sw, void *C, int64_t M, int64_t N, int64_t K, int out_f32,
+                       void *stream);
+
 /* W4A4: NVFP4 activations (Aq [M,K/2], As [M,K/16], Sa) under NVFP4 weights.
    Exact E4M3 route (hardware::exec docs, module description and
    fp4_fallback): both operands' codes converted by the E2M1 -> E4M3 bit
