@@ -159,6 +159,10 @@ def main():
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
     out = {}
+    # the secondary legs (everything but the headline) take at least 20 timed
+    # calls after at least 10 warm-up calls whatever --steps / --warmup say, so
+    # a short headline run does not leave them on the clock ramp
+    s2, w2 = max(args.steps, 20), max(args.warmup, 10)
 
     def todev(a):
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
@@ -220,7 +224,7 @@ def main():
             Cd = torch.empty((Mi, N), dtype=torch.bfloat16, device=dev)
             wsp = mg.workspace(mg.mgemm_workspace_bytes(mg.OP_W4A8, Mi, N, K), "w4a8")
             call = lambda i: mg.mgemm_w4a8(aq, atok, wq[i % copies], ws[i % copies], Sw, Cd, ws=wsp)  # noqa: E731
-            ms = timed(torch, call, max(args.steps, 40), args.warmup, stream)
+            ms = timed(torch, call, max(args.steps, 40), w2, stream)
             nbytes = N * K // 2 + N * K // 16 + Mi * K + 4 * Mi + 2 * Mi * N
             gbps = nbytes / (ms * 1e-3) / 1e9
             dec.append({"M": Mi, "us": round(ms * 1e3, 2), "GBps": round(gbps, 1),
@@ -238,9 +242,9 @@ def main():
         W = todev(b["w"].view(np.int16)).view(torch.bfloat16)
         Cb = torch.empty((Mb, N), dtype=torch.bfloat16, device=dev)
         if args.only != "bf16_grad":
-            ms = timed(torch, lambda i: mg.mgemm_bf16(A, W, Cb), args.steps, args.warmup, stream)
+            ms = timed(torch, lambda i: mg.mgemm_bf16(A, W, Cb), s2, w2, stream)
             tf = 2.0 * Mb * N * K / (ms * 1e-3) / 1e12
-            ms_t = timed(torch, lambda i: torch.matmul(A, W.t()), args.steps, args.warmup, stream)
+            ms_t = timed(torch, lambda i: torch.matmul(A, W.t()), s2, w2, stream)
             tf_t = 2.0 * Mb * N * K / (ms_t * 1e-3) / 1e12
             out["bf16"] = {"M": Mb, "N": N, "K": K, "ms": round(ms, 4), "tflops": round(tf, 1),
                            "frac_bf16_peak": round(tf / PEAK["bf16"], 4),
@@ -249,10 +253,8 @@ def main():
         dY = Cb.normal_()
         dX = torch.empty((Mb, K), dtype=torch.bfloat16, device=dev)
         dW = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
-        ms_d = timed(torch, lambda i: mg.mgemm_bf16_dgrad(dY, W, dX), max(5, args.steps // 4),
-                     min(args.warmup, 10), stream)
-        ms_w = timed(torch, lambda i: mg.mgemm_bf16_wgrad(dY, A, dW), max(5, args.steps // 4),
-                     min(args.warmup, 10), stream)
+        ms_d = timed(torch, lambda i: mg.mgemm_bf16_dgrad(dY, W, dX), s2, w2, stream)
+        ms_w = timed(torch, lambda i: mg.mgemm_bf16_wgrad(dY, A, dW), s2, w2, stream)
         fl = 2.0 * Mb * N * K
         out["bf16_grad"] = {"M": Mb, "N": N, "K": K, "dgrad_ms": round(ms_d, 4),
                             "dgrad_tflops": round(fl / (ms_d * 1e-3) / 1e12, 1),
@@ -271,18 +273,29 @@ def main():
         call = lambda i: mg.mgemm_moe_mxfp8_glu(dm["xq"], dm["xs"], dm["ids"], dm["tw"], dm["w13q"],  # noqa: E731
                                                 dm["w13s"], dm["w2q"], dm["w2s"], o, ws=wsp)
         if args.only != "moe_decode":
-            ms = timed(torch, call, max(3, args.steps // 2), min(args.warmup, 10), stream)
+            ms = timed(torch, call, s2, w2, stream)
             fl = 2.0 * T * topk * (H * 2 * I + I * H)
             tf = fl / (ms * 1e-3) / 1e12
             out["moe"] = {"T": T, "H": H, "I": I, "E": E, "topk": topk, "ms": round(ms, 3),
                           "tflops": round(tf, 1), "frac_fp8_peak": round(tf / PEAK["fp8"], 4)}
+            # the same call routed from the router logits inside the call
+            lgf = todev(synth.moe_logits(T, E, seed=0))
+            fid = torch.empty((T, topk), dtype=torch.int32, device=dev)
+            fw = torch.empty((T, topk), dtype=torch.float32, device=dev)
+            callf = lambda i: mg.mgemm_moe_mxfp8_glu_logits(  # noqa: E731
+                dm["xq"], dm["xs"], lgf, topk, dm["w13q"], dm["w13s"], dm["w2q"], dm["w2s"], o,
+                fid, fw, ws=wsp)
+            msf = timed(torch, callf, s2, w2, stream)
+            out["moe_fused_route"] = [{"T": T, "ms": round(msf, 3), "tflops": round(fl / (msf * 1e-3) / 1e12, 1),
+                                       "what": "routing from FP32 logits inside the call"}]
+            del fid, fw
         # the router top-k that produces such ids and weights (FP32 logits)
         if args.only != "moe_decode":
             lg = todev(synth.moe_logits(T, E, seed=0))
             rids = torch.empty((T, topk), dtype=torch.int32, device=dev)
             rw = torch.empty((T, topk), dtype=torch.float32, device=dev)
             callr = lambda i: mg.mgemm_moe_route_topk(lg, topk, rids, rw)  # noqa: E731
-            us = timed(torch, callr, max(20, args.steps), min(args.warmup, 20), stream) * 1e3
+            us = timed(torch, callr, s2, w2, stream) * 1e3
             rb = T * E * 4 + T * topk * 8
             out["moe_route"] = {"T": T, "E": E, "topk": topk, "us": round(us, 2),
                                 "GBps": round(rb / us / 1e3, 1)}
@@ -302,15 +315,23 @@ def main():
             calld = lambda i, sls=sls, od=od, wsd=wsd: mg.mgemm_moe_mxfp8_glu(  # noqa: E731
                 sls[i % len(sls)]["xq"], sls[i % len(sls)]["xs"], sls[i % len(sls)]["ids"],
                 sls[i % len(sls)]["tw"], dm["w13q"], dm["w13s"], dm["w2q"], dm["w2s"], od, ws=wsd)
-            steps_d = len(sls) * max(1, max(20, args.steps) // len(sls))
-            us = timed(torch, calld, steps_d, min(args.warmup, 20), stream) * 1e3
+            steps_d = len(sls) * max(1, s2 // len(sls))
+            us = timed(torch, calld, steps_d, w2, stream) * 1e3
             ne = np.mean([len(np.unique(m["ids"][g * Td:(g + 1) * Td])) for g in range(groups)])
             nbytes = (ne * 3 * I * H * (1 + 1 / 32)                  # expert weights, codes + scales
                       + Td * H * (1 + 1 / 32) + Td * topk * 8 + 2 * Td * H)   # x, routing, out
-            dec.append({"T": Td, "experts": round(float(ne), 2), "token_groups": groups,
-                        "us": round(us, 2), "bytes": int(nbytes),
-                        "GBps": round(nbytes / us / 1e3, 1),
-                        "frac_hbm": round(nbytes / us / 1e3 / PEAK["hbm"], 4)})
+            row = {"T": Td, "experts": round(float(ne), 2), "token_groups": groups,
+                   "us": round(us, 2), "bytes": int(nbytes), "GBps": round(nbytes / us / 1e3, 1),
+                   "frac_hbm": round(nbytes / us / 1e3 / PEAK["hbm"], 4)}
+            # the same calls routed from the router logits inside the call
+            lgs = [todev(synth.moe_logits(T, E, seed=0)[g * Td:(g + 1) * Td]) for g in range(groups)]
+            fid = torch.empty((Td, topk), dtype=torch.int32, device=dev)
+            fw = torch.empty((Td, topk), dtype=torch.float32, device=dev)
+            callf = lambda i, sls=sls, od=od, wsd=wsd, lgs=lgs: mg.mgemm_moe_mxfp8_glu_logits(  # noqa: E731
+                sls[i % len(sls)]["xq"], sls[i % len(sls)]["xs"], lgs[i % len(lgs)], topk,
+                dm["w13q"], dm["w13s"], dm["w2q"], dm["w2s"], od, fid, fw, ws=wsd)
+            row["fused_route_us"] = round(timed(torch, callf, steps_d, w2, stream) * 1e3, 2)
+            dec.append(row)
         out["moe_decode"] = dec
         del dm, o
         torch.cuda.empty_cache()
@@ -327,7 +348,7 @@ def main():
         call4 = lambda i: mg.mgemm_moe_nvfp4_glu(  # noqa: E731
             d4["xq"], d4["xs"], sx, d4["ids"], d4["tw"], d4["w13q"], d4["w13s"], d4["Sw13"],
             d4["w2q"], d4["w2s"], d4["Sw2"], sh, o4, ws=ws4)
-        ms = timed(torch, call4, max(3, args.steps // 2), min(args.warmup, 10), stream)
+        ms = timed(torch, call4, s2, w2, stream)
         fl = 2.0 * T * topk * (H * 2 * I + I * H)
         tf = fl / (ms * 1e-3) / 1e12
         fmas = T * topk * (H * 2 * I + I * H) / 16          # per-group scale FMAs
@@ -403,6 +424,7 @@ def main():
         "moe_decode": out.get("moe_decode"),
         "moe_nvfp4": out.get("moe_nvfp4"),
         "moe_route": out.get("moe_route"),
+        "moe_fused_route": out.get("moe_fused_route"),
         "device": torch.cuda.get_device_properties(0).gcnArchName,
         "kernel_src": src_hash("gemm_w4a4.hip", "common.h"),
     }
