@@ -99,7 +99,7 @@ def write_traffic(fetch_dir, write_dir, calib_mib):
     known size from the same run (it reads and writes calib_mib MiB)."""
     fetch, write = _pmc_means(fetch_dir, "FETCH_SIZE"), _pmc_means(write_dir, "WRITE_SIZE")
     pick = lambda d, sub: [v for k, v in d.items() if sub in k]  # noqa: E731
-    kf, kw = pick(fetch, "w4a4_fp8route_kernel"), pick(write, "w4a4_fp8route_kernel")
+    kf, kw = pick(fetch, "w4a4_fp8route"), pick(write, "w4a4_fp8route")
     cf, cw = pick(fetch, "MulFunctor"), pick(write, "MulFunctor")
     if not (kf and kw and cf and cw):
         raise SystemExit(f"kernels not found: {sorted(fetch)}")
@@ -286,7 +286,13 @@ def main():
                 dm["xq"], dm["xs"], lgf, topk, dm["w13q"], dm["w13s"], dm["w2q"], dm["w2s"], o,
                 fid, fw, ws=wsp)
             msf = timed(torch, callf, s2, w2, stream)
+            # the same routing as two calls: the router, then the MoE on its ids
+            callu = lambda i: (mg.mgemm_moe_route_topk(lgf, topk, fid, fw),  # noqa: E731
+                               mg.mgemm_moe_mxfp8_glu(dm["xq"], dm["xs"], fid, fw, dm["w13q"],
+                                                      dm["w13s"], dm["w2q"], dm["w2s"], o, ws=wsp))
+            msu = timed(torch, callu, s2, w2, stream)
             out["moe_fused_route"] = [{"T": T, "ms": round(msf, 3), "tflops": round(fl / (msf * 1e-3) / 1e12, 1),
+                                       "router_then_moe_ms": round(msu, 3),
                                        "what": "routing from FP32 logits inside the call"}]
             del fid, fw
         # the router top-k that produces such ids and weights (FP32 logits)
@@ -331,6 +337,11 @@ def main():
                 sls[i % len(sls)]["xq"], sls[i % len(sls)]["xs"], lgs[i % len(lgs)], topk,
                 dm["w13q"], dm["w13s"], dm["w2q"], dm["w2s"], od, fid, fw, ws=wsd)
             row["fused_route_us"] = round(timed(torch, callf, steps_d, w2, stream) * 1e3, 2)
+            callu = lambda i, sls=sls, od=od, wsd=wsd, lgs=lgs: (  # noqa: E731
+                mg.mgemm_moe_route_topk(lgs[i % len(lgs)], topk, fid, fw),
+                mg.mgemm_moe_mxfp8_glu(sls[i % len(sls)]["xq"], sls[i % len(sls)]["xs"], fid, fw,
+                                       dm["w13q"], dm["w13s"], dm["w2q"], dm["w2s"], od, ws=wsd))
+            row["router_then_moe_us"] = round(timed(torch, callu, steps_d, w2, stream) * 1e3, 2)
             dec.append(row)
         out["moe_decode"] = dec
         del dm, o

@@ -183,9 +183,175 @@ __global__ __launch_bounds__(512, 2) void w4a4_fp8route_kernel(W4A4Args p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// The same route on a 256 x 256 tile (M and N above 128): 512 threads (8
+// waves, 4 x 2), wave tile 64 x 128 (2 x 4 blocks of 32 x 32).  Per stage a
+// thread converts 32 codes of A and 32 of W, which now serve a wave's 8
+// blocks per group instead of 2, and a wave reads 2 A and 4 W code operands
+// and 2 + 4 scale operands per group for 8 blocks (12 LDS reads, half of the
+// 128 x 128 tile's per block).  One workgroup per CU (2 waves per SIMD; the
+// accumulators of 8 blocks take 128 registers).  Every FP32 rounding is the
+// 128 x 128 kernel's (the same group terms in the same order).
+namespace big {
+
+constexpr int BM = 256, BN = 256;
+constexpr int GPS = 4;
+__device__ __forceinline__ int coff(int row, int g, int h) {
+  return ((((row >> 5) * GPS + g) * 64) + h * 32 + (row & 31)) * 8;
+}
+struct Stage {
+  uint8_t code[2][BM * GPS * 16];   // A, W codes as E4M3 in MFMA operand order
+  uint64_t sc[2][GPS * BM];         // [g][row]: raw scale byte at K = 0, zeros above
+};
+struct StageRegs {
+  u32x4 a, w;        // 32 codes of one A row and one W row (groups 2q, 2q+1)
+  uint32_t s0, s1;   // scale bytes of groups (0, 1) and (2, 3) of one row
+};
+
+__device__ __forceinline__ void load_stage(const W4A4Args &p, int m0, int n0, int g0, int G,
+                                           int tid, StageRegs &r) {
+  const int64_t rowb = p.K / 2, rows = p.K / 16;
+  const int row = tid >> 1, q = tid & 1;
+  const int g = g0 + 2 * q;
+  const int gs = g < G ? g : G - 2;          // in-bounds address (G even)
+  {
+    const int ga = m0 + row < p.M ? m0 + row : p.M - 1;
+    const int gw = n0 + row < p.N ? n0 + row : p.N - 1;
+    r.a = *(const u32x4 *)(p.aq + (int64_t)ga * rowb + (int64_t)gs * 8);
+    r.w = *(const u32x4 *)(p.wq + (int64_t)gw * rowb + (int64_t)gs * 8);
+  }
+  {
+    // threads 0..255 fetch A rows' scales, 256..511 W rows'
+    const int op = tid >> 8, srow = tid & 255;
+    const uint8_t *base = op == 0 ? p.as : p.ws;
+    const int R = op == 0 ? p.M : p.N, o = op == 0 ? m0 : n0;
+    const int grow = o + srow < R ? o + srow : R - 1;
+    const uint16_t *s16 = (const uint16_t *)(base + (int64_t)grow * rows);
+    r.s0 = s16[(g0 < G ? g0 : G - 2) >> 1];
+    r.s1 = s16[(g0 + 2 < G ? g0 + 2 : G - 2) >> 1];
+  }
+}
+
+__device__ __forceinline__ void store_codes(uint8_t *c, int row, int q, u32x4 v) {
+  const uint64_t e0 = nvfp4x8_to_e4m3x8(v[0]), e1 = nvfp4x8_to_e4m3x8(v[1]);
+  const uint64_t e2 = nvfp4x8_to_e4m3x8(v[2]), e3 = nvfp4x8_to_e4m3x8(v[3]);
+  *(uint64_t *)(c + coff(row, 2 * q, 0)) = e0;
+  *(uint64_t *)(c + coff(row, 2 * q, 1)) = e1;
+  *(uint64_t *)(c + coff(row, 2 * q + 1, 0)) = e2;
+  *(uint64_t *)(c + coff(row, 2 * q + 1, 1)) = e3;
+}
+
+__device__ __forceinline__ void store_stage(Stage &s, int tid, const StageRegs &r, int g0, int G) {
+  const int row = tid >> 1, q = tid & 1;
+  const bool in = g0 + 2 * q < G;
+  store_codes(s.code[0], row, q, in ? r.a : u32x4{0, 0, 0, 0});
+  store_codes(s.code[1], row, q, in ? r.w : u32x4{0, 0, 0, 0});
+  const uint32_t w = (g0 < G ? r.s0 : 0u) | ((g0 + 2 < G ? r.s1 : 0u) << 16);
+  const int op = tid >> 8, srow = tid & 255;
+#pragma unroll
+  for (int g = 0; g < GPS; ++g) s.sc[op][g * BM + srow] = (w >> (8 * g)) & 0xFFu;
+}
+
+__global__ __launch_bounds__(512, 1) void w4a4_fp8route_big(W4A4Args p) {
+  __shared__ __attribute__((aligned(16))) Stage lds[2];
+  __shared__ uint64_t zero8;   // the A-side scale operand of lanes h = 1
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, h = lane >> 5;
+  int tm, tn;
+  xcd_tile(blockIdx.x, (p.M + BM - 1) / BM, (p.N + BN - 1) / BN, tm, tn);
+  const int n0 = tn * BN, m0 = tm * BM;
+  const int G = p.K / 16;
+  const int S = (G + GPS - 1) / GPS;
+
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{0};
+  const f32x16 zero = {0};
+
+  auto compute = [&](const Stage &cur) {
+    // scale operands: lane (row, h = 0) holds its row's raw scale byte at
+    // K = 0 and zeros elsewhere; A-side lanes h = 1 read zeros, so the K = 16
+    // product is exactly s_a * s_w (a NaN scale still yields NaN)
+    const uint8_t *pa = cur.code[0] + coff(wm * 64, 0, 0) + 8 * lane;
+    const uint8_t *pw = cur.code[1] + coff(wn * 128, 0, 0) + 8 * lane;
+#pragma unroll
+    for (int g = 0; g < GPS; ++g) {
+      uint64_t a[2], w[4], sa[2], sw[4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        a[i] = *(const uint64_t *)(pa + (i * GPS + g) * 512);
+        sa[i] = h ? zero8 : cur.sc[0][g * BM + wm * 64 + 32 * i + l32];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        w[j] = *(const uint64_t *)(pw + (j * GPS + g) * 512);
+        sw[j] = cur.sc[1][g * BM + wn * 128 + 32 * j + l32];
+      }
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
+        const int i = b >> 2, j = b & 3;
+        const f32x16 c = mfma_fp8(sa[i], sw[j], zero);
+        const f32x16 pp = mfma_fp8(a[i], w[j], zero);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(c[r], pp[r], acc[i][j][r]);
+      }
+    }
+  };
+  if (tid == 0) zero8 = 0;
+  StageRegs r0, r1;
+  load_stage(p, m0, n0, 0, G, tid, r0);
+  load_stage(p, m0, n0, GPS, G, tid, r1);
+  store_stage(lds[0], tid, r0, 0, G);
+  __syncthreads();
+  load_stage(p, m0, n0, 2 * GPS, G, tid, r0);
+  for (int s = 0; s < S; s += 2) {
+    // lds[0] holds stage s, r1 stage s+1, r0 stage s+2 (in flight)
+    compute(lds[0]);
+    store_stage(lds[1], tid, r1, (s + 1) * GPS, G);
+    __syncthreads();
+    load_stage(p, m0, n0, (s + 3) * GPS, G, tid, r1);
+    if (s + 1 >= S) break;
+    compute(lds[1]);
+    store_stage(lds[0], tid, r0, (s + 2) * GPS, G);
+    __syncthreads();
+    load_stage(p, m0, n0, (s + 4) * GPS, G, tid, r0);
+  }
+
+  const float gsc = *p.Sa * *p.Sw * 4096.0f;  // c_g lacks the folded 2^6 * 2^6
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int col = n0 + wn * 128 + j * 32 + l32;
+    if (col >= p.N) continue;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm * 64 + i * 32 + acc_row(r, lane);
+        if (row >= p.M) continue;
+        const float v = acc[i][j][r] * gsc;
+        if (p.out_f32)
+          ((float *)p.C)[(int64_t)row * p.N + col] = v;
+        else
+          ((uint16_t *)p.C)[(int64_t)row * p.N + col] = (uint16_t)f32_to_bf16_rne(v);
+      }
+  }
+}
+
+}  // namespace big
+
 }  // namespace
 
 hipError_t launch_w4a4(const W4A4Args &p, hipStream_t stream) {
+  // the 256 x 256 tile for large products; small ones keep the 128 x 128
+  // tile (less padding, more workgroups)
+  if (p.M > 128 && p.N > 128) {
+    dim3 grid(((p.N + big::BN - 1) / big::BN) * ((p.M + big::BM - 1) / big::BM));
+    hipLaunchKernelGGL(big::w4a4_fp8route_big, grid, dim3(512), 0, stream, p);
+    return hipGetLastError();
+  }
   dim3 grid(((p.N + BN - 1) / BN) * ((p.M + BM - 1) / BM));
   hipLaunchKernelGGL(w4a4_fp8route_kernel, grid, dim3(512), 0, stream, p);
   return hipGetLastError();

@@ -34,6 +34,7 @@ constexpr int BM = 128;       // rows (routing entries) per tile
 constexpr int BNI = 64;       // intermediate columns per gate/up tile (x2 rows of w13)
 constexpr int BNH = 128;      // hidden columns per down tile
 constexpr int BK = 64;        // K per LDS stage (two 32-element scale blocks)
+constexpr int CSTRIDE = 32;   // uint32s between two experts' row counters
 
 struct Layout {
   size_t counts, offs, meta, sorted, pos, wsorted, tile_e, tile_r, tile_n, hq, hs, y, total;
@@ -49,7 +50,7 @@ Layout layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk, bool fp4
   L.R = (int)(T * topk);
   L.maxtiles = (int)((L.R + BM - 1) / BM + E);
   size_t o = 0;
-  L.counts = o; o += up256(sizeof(uint32_t) * (size_t)E);
+  L.counts = o; o += up256(sizeof(uint32_t) * CSTRIDE * (size_t)E);   // one 128-byte line each
   L.offs = o;   o += up256(sizeof(int32_t) * (size_t)E);
   L.meta = o;   o += up256(sizeof(int32_t) * 4);                 // [0] = number of tiles
   L.sorted = o; o += up256(sizeof(int32_t) * (size_t)L.R);
@@ -66,9 +67,12 @@ Layout layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk, bool fp4
 }
 
 // ---------------------------------------------------------------- routing
+// Expert e's row counter is counts[CSTRIDE * e]: one 128-byte line per
+// expert, so the workgroups' atomic reservations on different experts go to
+// different lines (and L2 channels) instead of queueing on two lines.
 __global__ void k_prep(uint32_t *counts, int E) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < E) counts[i] = 0u;
+  if (i < E) counts[CSTRIDE * i] = 0u;
 }
 
 // rank of each entry within its expert (arrival order); out-of-range ids are
@@ -86,7 +90,7 @@ __global__ __launch_bounds__(1024) void k_count(const int32_t *ids, int R, int E
   const bool ok = e >= 0 && e < E;
   const uint32_t lr = ok ? atomicAdd(&s_cnt[e], 1u) : 0u;
   __syncthreads();
-  if (tid < E && s_cnt[tid] != 0u) s_base[tid] = atomicAdd(&counts[tid], s_cnt[tid]);
+  if (tid < E && s_cnt[tid] != 0u) s_base[tid] = atomicAdd(&counts[CSTRIDE * tid], s_cnt[tid]);
   __syncthreads();
   if (i < R) rank[i] = ok ? (int32_t)(s_base[e] + lr) : -1;
 }
@@ -103,7 +107,7 @@ __global__ __launch_bounds__(256) void k_scan(const uint32_t *counts, int E, int
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
     const int e = tid * PER + k;
-    const int c = e < E ? (int)counts[e] : 0;
+    const int c = e < E ? (int)counts[CSTRIDE * e] : 0;
     rows[k] = c;
     tiles[k] = (c + BM - 1) / BM;
     r += c;
@@ -717,16 +721,22 @@ __global__ __launch_bounds__(256) void k_dec(MoeArgs p, const int32_t *meta, con
 // probabilities (equal logits: the lower id first).  Slot j's id and weight
 // go to ids[j], w[j] and, when given, to the LDS copies lids[j], lw[j].
 template <int PER>
-__device__ __forceinline__ void route_token(const float *row, int E, int topk, int lane,
-                                            int32_t *ids, float *w, int32_t *lids, float *lw) {
-  float v[PER], ex[PER];
-  float m = -__builtin_inff();
+__device__ __forceinline__ void load_logits(const float *row, int E, int lane, float (&v)[PER]) {
 #pragma unroll
   for (int q = 0; q < PER; ++q) {
     const int e = lane + 64 * q;
     v[q] = e < E ? row[e] : -__builtin_inff();
-    m = fmaxf(m, v[q]);
   }
+}
+
+// the same on logits already loaded (this lane's v[q] = logit lane + 64 q)
+template <int PER>
+__device__ __forceinline__ void route_loaded(float (&v)[PER], int E, int topk, int lane,
+                                             int32_t *ids, float *w, int32_t *lids, float *lw) {
+  float ex[PER];
+  float m = -__builtin_inff();
+#pragma unroll
+  for (int q = 0; q < PER; ++q) m = fmaxf(m, v[q]);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
   float s = 0.0f;
@@ -775,6 +785,14 @@ __device__ __forceinline__ void route_token(const float *row, int E, int topk, i
   }
 }
 
+template <int PER>
+__device__ __forceinline__ void route_token(const float *row, int E, int topk, int lane,
+                                            int32_t *ids, float *w, int32_t *lids, float *lw) {
+  float v[PER];
+  load_logits<PER>(row, E, lane, v);
+  route_loaded<PER>(v, E, topk, lane, ids, w, lids, lw);
+}
+
 // the router alone: one wave per token
 template <int PER>
 __global__ __launch_bounds__(256) void k_topk_softmax(const float *logits, int T, int E, int topk,
@@ -792,30 +810,43 @@ __global__ __launch_bounds__(256) void k_topk_softmax(const float *logits, int T
 // expert in LDS, reserves each expert's run of ranks with one global atomic,
 // and writes each entry's rank -- what k_topk_softmax then k_count compute,
 // without the ids' round trip through a second launch.
-constexpr int RT_TOK = 16;   // tokens per workgroup (4 waves x 4)
+constexpr int RT_TOK = 64;   // tokens per workgroup (16 waves x 4)
 template <int PER>
-__global__ __launch_bounds__(256) void k_count_logits(const float *logits, int T, int E, int topk,
+__global__ __launch_bounds__(1024) void k_count_logits(const float *logits, int T, int E, int topk,
                                                       int32_t *ids, float *tw, uint32_t *counts,
                                                       int32_t *rank) {
   __shared__ uint32_t s_cnt[1024], s_base[1024];
-  __shared__ int32_t s_ids[RT_TOK * 16];
+  __shared__ int32_t s_ids[RT_TOK * 16];   // topk <= 16
   __shared__ float s_w[RT_TOK * 16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = blockIdx.x * RT_TOK;
   const int nt = T - t0 < RT_TOK ? T - t0 : RT_TOK;
-  for (int e = tid; e < E; e += 256) s_cnt[e] = 0u;
-  for (int i = wave; i < nt; i += 4) {
-    const int64_t t = t0 + i;
-    route_token<PER>(logits + t * E, E, topk, lane, ids + t * topk, tw + t * topk,
-                     s_ids + i * topk, s_w + i * topk);
+  for (int e = tid; e < E; e += 1024) s_cnt[e] = 0u;
+  // this wave's tokens i = wave + 16 q: every logit requested before the
+  // first is used (one memory latency, not one per token)
+  constexpr int TPW = RT_TOK / 16;
+  float v[TPW][PER];
+#pragma unroll
+  for (int q = 0; q < TPW; ++q) {
+    const int i = wave + 16 * q;
+    load_logits<PER>(logits + (int64_t)(t0 + (i < nt ? i : 0)) * E, E, lane, v[q]);
+  }
+#pragma unroll
+  for (int q = 0; q < TPW; ++q) {
+    const int i = wave + 16 * q;
+    if (i < nt) {
+      const int64_t t = t0 + i;
+      route_loaded<PER>(v[q], E, topk, lane, ids + t * topk, tw + t * topk, s_ids + i * topk,
+                        s_w + i * topk);
+    }
   }
   __syncthreads();
-  const int n = nt * topk;            // entries of this workgroup (at most 256)
+  const int n = nt * topk;            // entries of this workgroup (at most 1024)
   const int e = tid < n ? s_ids[tid] : -1;
   const uint32_t lr = tid < n ? atomicAdd(&s_cnt[e], 1u) : 0u;
   __syncthreads();
-  for (int x = tid; x < E; x += 256)
-    if (s_cnt[x] != 0u) s_base[x] = atomicAdd(&counts[x], s_cnt[x]);
+  for (int x = tid; x < E; x += 1024)
+    if (s_cnt[x] != 0u) s_base[x] = atomicAdd(&counts[CSTRIDE * x], s_cnt[x]);
   __syncthreads();
   if (tid < n) rank[(int64_t)t0 * topk + tid] = (int32_t)(s_base[e] + lr);
 }
@@ -986,13 +1017,13 @@ hipError_t launch_moe(const MoeArgs &p, hipStream_t stream) {
     int32_t *ids = (int32_t *)p.ids;
     float *tw = (float *)p.tw;
     if (p.E <= 64)
-      hipLaunchKernelGGL(k_count_logits<1>, gr, dim3(256), 0, stream, p.logits, p.T, p.E, p.topk,
+      hipLaunchKernelGGL(k_count_logits<1>, gr, dim3(1024), 0, stream, p.logits, p.T, p.E, p.topk,
                          ids, tw, counts, pos);
     else if (p.E <= 256)
-      hipLaunchKernelGGL(k_count_logits<4>, gr, dim3(256), 0, stream, p.logits, p.T, p.E, p.topk,
+      hipLaunchKernelGGL(k_count_logits<4>, gr, dim3(1024), 0, stream, p.logits, p.T, p.E, p.topk,
                          ids, tw, counts, pos);
     else
-      hipLaunchKernelGGL(k_count_logits<16>, gr, dim3(256), 0, stream, p.logits, p.T, p.E, p.topk,
+      hipLaunchKernelGGL(k_count_logits<16>, gr, dim3(1024), 0, stream, p.logits, p.T, p.E, p.topk,
                          ids, tw, counts, pos);
   }
   hipLaunchKernelGGL(k_scan, dim3(1), dim3(256), 0, stream, counts, p.E, offs, meta, tile_e,

@@ -48,11 +48,12 @@ def test_window_bound_groups_and_scales():
     # group 0 loses 7 * 2^-12, group 1 (exponent sum -2, last bit 2^-15) nothing
     assert fp8_window_bound(a, w) == 7 * 2.0 ** -12
     assert fp8_window_bound(a, w, gscale=np.array([3.0, 0.5])) == 3 * 7 * 2.0 ** -12
-    # a zero operand takes part in the exponent maximum (-6), which can only
-    # coarsen the bit: a zero next to 448 raises it here
+    # a product with a zero operand does not place the window: a zero next to
+    # 448 leaves the one real product exact; an all-zero group loses nothing
     a = np.array([0.0, 2.0 ** -9] + [0.0] * 6)
     w = np.array([448.0, 2.0 ** -9] + [0.0] * 6)
-    assert fp8_window_bound(a, w) == 2.0 ** -18
+    assert fp8_window_bound(a, w) == 0.0
+    assert fp8_window_bound(np.zeros(8), np.full(8, 448.0)) == 0.0
     # leading dimensions
     assert fp8_window_bound(np.stack([a, a]), w).shape == (2,)
 
