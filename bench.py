@@ -16,7 +16,11 @@ oracle timed on the host on a bounded sample of the same workload
 (`cpu_baseline`), a sampled parity check of the timed output against the
 oracle, the W4A8 swap-AB decode shapes (M = 1, 8, 32, 128; GB/s against the
 HBM roofline, weights rotated over 8 copies so the 256 MB Infinity Cache
-cannot serve them), and the BF16 and MXFP8-MoE configurations.
+cannot serve them), the small-M W4A16 shapes (M = 1, 16, 128, likewise), and
+the BF16 and MXFP8-MoE configurations.  Decode-sized calls are timed as HIP
+graphs of back-to-back calls replayed on the device ("us"; the per-call
+launch cost of the Python binding exceeds such a kernel's duration), with
+the eager per-call loop beside them ("eager_us").
 
 Only one GPU is supported: --gpus N with N > 1 exits with a message.
 """
@@ -44,7 +48,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quick", action="store_true", help="headline kernel only")
     ap.add_argument("--only", default="",
-                    help="w4a4|w4a8|bf16|bf16_grad|moe|moe_decode|moe_nvfp4 (profiling runs)")
+                    help="w4a4|w4a8|w4a16|bf16|bf16_grad|moe|moe_decode|moe_nvfp4 (profiling runs)")
     ap.add_argument("--moe-dec-tokens", default="1,16",
                     help="token counts of the decode-sized MoE calls")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -137,6 +141,37 @@ def timed(torch, fn, steps, warmup, stream):
     return e0.elapsed_time(e1) / steps  # ms per call
 
 
+def timed_graph(torch, fn, calls, steps, warmup):
+    """Device time per call of fn(0) .. fn(calls - 1) captured back to back
+    in one HIP graph and replayed `steps` times: the launch cost of the
+    Python binding (about 15-20 us per call, more than a decode-sized
+    kernel takes) is paid once at capture, as in a graph-replayed decode
+    step.  Arguments must not allocate inside the calls (workspaces passed
+    in)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(calls):
+            fn(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(calls):
+            fn(i)
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (steps * calls)  # ms per call
+
+
 def main():
     args = parse()
     if args.traffic:
@@ -224,13 +259,41 @@ def main():
             Cd = torch.empty((Mi, N), dtype=torch.bfloat16, device=dev)
             wsp = mg.workspace(mg.mgemm_workspace_bytes(mg.OP_W4A8, Mi, N, K), "w4a8")
             call = lambda i: mg.mgemm_w4a8(aq, atok, wq[i % copies], ws[i % copies], Sw, Cd, ws=wsp)  # noqa: E731
-            ms = timed(torch, call, max(args.steps, 40), w2, stream)
+            ms = timed_graph(torch, call, 2 * copies, max(args.steps, 20), w2)
+            ms_e = timed(torch, call, max(args.steps, 40), w2, stream)
             nbytes = N * K // 2 + N * K // 16 + Mi * K + 4 * Mi + 2 * Mi * N
             gbps = nbytes / (ms * 1e-3) / 1e9
             dec.append({"M": Mi, "us": round(ms * 1e3, 2), "GBps": round(gbps, 1),
                         "frac_hbm": round(gbps / PEAK["hbm"], 4), "bytes": nbytes,
-                        "tflops": round(2.0 * Mi * N * K / (ms * 1e-3) / 1e12, 2)})
+                        "tflops": round(2.0 * Mi * N * K / (ms * 1e-3) / 1e12, 2),
+                        "eager_us": round(ms_e * 1e3, 2)})
         out["decode"] = dec
+        del wq, ws
+        torch.cuda.empty_cache()
+
+    # -------------------------------------------------- W4A16 decode shapes
+    if args.only in ("", "w4a16") and not args.quick:
+        w = synth.w4a16(1, N, K, seed=0)  # the weight tensor is shared by every M
+        copies = 8
+        wq = [todev(w["wq"]) for _ in range(copies)]
+        ws = [todev(w["ws"]) for _ in range(copies)]
+        Sw = f32(w["Sw"])
+        dec = []
+        for Mi in (1, 16, 128):
+            a = todev(synth.to_bf16_bits(synth.normal((Mi, K), 1.0, Mi, synth.ROLE_A)).view(np.int16))
+            a = a.view(torch.bfloat16)
+            Cd = torch.empty((Mi, N), dtype=torch.bfloat16, device=dev)
+            wsp = mg.workspace(mg.mgemm_workspace_bytes(mg.OP_W4A16, Mi, N, K), "w4a16")
+            call = lambda i: mg.mgemm_w4a16(a, wq[i % copies], ws[i % copies], Sw, Cd, ws=wsp)  # noqa: E731
+            ms = timed_graph(torch, call, 2 * copies, max(args.steps, 20), w2)
+            ms_e = timed(torch, call, max(args.steps, 40), w2, stream)
+            nbytes = N * K // 2 + N * K // 16 + 2 * Mi * K + 2 * Mi * N
+            gbps = nbytes / (ms * 1e-3) / 1e9
+            dec.append({"M": Mi, "us": round(ms * 1e3, 2), "GBps": round(gbps, 1),
+                        "frac_hbm": round(gbps / PEAK["hbm"], 4), "bytes": nbytes,
+                        "tflops": round(2.0 * Mi * N * K / (ms * 1e-3) / 1e12, 2),
+                        "eager_us": round(ms_e * 1e3, 2)})
+        out["w4a16_decode"] = dec
         del wq, ws
         torch.cuda.empty_cache()
 
@@ -322,13 +385,14 @@ def main():
                 sls[i % len(sls)]["xq"], sls[i % len(sls)]["xs"], sls[i % len(sls)]["ids"],
                 sls[i % len(sls)]["tw"], dm["w13q"], dm["w13s"], dm["w2q"], dm["w2s"], od, ws=wsd)
             steps_d = len(sls) * max(1, s2 // len(sls))
-            us = timed(torch, calld, steps_d, w2, stream) * 1e3
+            us = timed_graph(torch, calld, len(sls), max(1, s2 // len(sls)), w2) * 1e3
+            us_e = timed(torch, calld, steps_d, w2, stream) * 1e3
             ne = np.mean([len(np.unique(m["ids"][g * Td:(g + 1) * Td])) for g in range(groups)])
             nbytes = (ne * 3 * I * H * (1 + 1 / 32)                  # expert weights, codes + scales
                       + Td * H * (1 + 1 / 32) + Td * topk * 8 + 2 * Td * H)   # x, routing, out
             row = {"T": Td, "experts": round(float(ne), 2), "token_groups": groups,
                    "us": round(us, 2), "bytes": int(nbytes), "GBps": round(nbytes / us / 1e3, 1),
-                   "frac_hbm": round(nbytes / us / 1e3 / PEAK["hbm"], 4)}
+                   "frac_hbm": round(nbytes / us / 1e3 / PEAK["hbm"], 4), "eager_us": round(us_e, 2)}
             # the same calls routed from the router logits inside the call
             lgs = [todev(synth.moe_logits(T, E, seed=0)[g * Td:(g + 1) * Td]) for g in range(groups)]
             fid = torch.empty((Td, topk), dtype=torch.int32, device=dev)
@@ -336,12 +400,12 @@ def main():
             callf = lambda i, sls=sls, od=od, wsd=wsd, lgs=lgs: mg.mgemm_moe_mxfp8_glu_logits(  # noqa: E731
                 sls[i % len(sls)]["xq"], sls[i % len(sls)]["xs"], lgs[i % len(lgs)], topk,
                 dm["w13q"], dm["w13s"], dm["w2q"], dm["w2s"], od, fid, fw, ws=wsd)
-            row["fused_route_us"] = round(timed(torch, callf, steps_d, w2, stream) * 1e3, 2)
+            row["fused_route_us"] = round(timed_graph(torch, callf, len(sls), max(1, s2 // len(sls)), w2) * 1e3, 2)
             callu = lambda i, sls=sls, od=od, wsd=wsd, lgs=lgs: (  # noqa: E731
                 mg.mgemm_moe_route_topk(lgs[i % len(lgs)], topk, fid, fw),
                 mg.mgemm_moe_mxfp8_glu(sls[i % len(sls)]["xq"], sls[i % len(sls)]["xs"], fid, fw,
                                        dm["w13q"], dm["w13s"], dm["w2q"], dm["w2s"], od, ws=wsd))
-            row["router_then_moe_us"] = round(timed(torch, callu, steps_d, w2, stream) * 1e3, 2)
+            row["router_then_moe_us"] = round(timed_graph(torch, callu, len(sls), max(1, s2 // len(sls)), w2) * 1e3, 2)
             dec.append(row)
         out["moe_decode"] = dec
         del dm, o
@@ -429,6 +493,7 @@ def main():
         "mfma_roofline": out.get("mfma_roofline"),
         "parity_sample": par,
         "decode": out.get("decode"),
+        "w4a16_decode": out.get("w4a16_decode"),
         "bf16": out.get("bf16"),
         "bf16_grad": out.get("bf16_grad"),
         "moe": out.get("moe"),

@@ -68,7 +68,7 @@ def load() -> C.CDLL:
         "mgemm_plan_arch": (i32, [C.c_char_p, i32, i32, C.POINTER(_Plan)]),
         "mgemm_pair_name": (i32, [i32, i32, C.c_char_p, C.c_size_t]),
         "mgemm_bf16": (i32, [vp, vp, vp, i64, i64, i64, i32, vp]),
-        "mgemm_w4a16": (i32, [vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]),
+        "mgemm_w4a16": (i32, [vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, C.c_size_t, vp]),
         "mgemm_w4a8": (i32, [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, C.c_size_t, vp]),
         "mgemm_w4a8_noalloc": (i32, [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]),
         "mgemm_w4a4": (i32, [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]),
@@ -182,7 +182,7 @@ def mgemm_bf16(A: torch.Tensor, W: torch.Tensor, C_out: torch.Tensor, stream=Non
     return C_out
 
 
-def mgemm_w4a16(A, Wq, Ws, Sw, C_out, stream=None):
+def mgemm_w4a16(A, Wq, Ws, Sw, C_out, ws: Optional[torch.Tensor] = None, stream=None):
     M, K = A.shape
     N = Wq.shape[0]
     _need(A, "A", _BF16_T, (M, K))
@@ -190,9 +190,16 @@ def mgemm_w4a16(A, Wq, Ws, Sw, C_out, stream=None):
     _need(Ws, "Ws", _U8, (N, K // 16))
     _need(Sw, "Sw", _F32, numel=1)
     _need(C_out, "C", _C_T, (M, N))
+    need = mgemm_workspace_bytes(OP_W4A16, M, N, K)
+    if ws is None:
+        ws = workspace(need, "w4a16", stream)
+    if need and (ws is None or ws.numel() * ws.element_size() < need):
+        raise ValueError("w4a16: workspace too small")
+    wp = ws.data_ptr() if ws is not None else None
+    wb = ws.numel() * ws.element_size() if ws is not None else 0
     _check("mgemm_w4a16", load().mgemm_w4a16(A.data_ptr(), Wq.data_ptr(), Ws.data_ptr(),
                                              Sw.data_ptr(), C_out.data_ptr(), M, N, K,
-                                             _out_f32(C_out), _stream(stream)))
+                                             _out_f32(C_out), wp, wb, _stream(stream)))
     return C_out
 
 

@@ -187,14 +187,18 @@ int mgemm_bf16(const void *A, const void *W, void *C, int64_t M, int64_t N, int6
 }
 
 int mgemm_w4a16(const void *A, const void *Wq, const void *Ws, const float *Sw, void *C,
-                int64_t M, int64_t N, int64_t K, int out_f32, void *stream) {
+                int64_t M, int64_t N, int64_t K, int out_f32, void *ws, size_t ws_bytes,
+                void *stream) {
   if (!A || !Wq || !Ws || !Sw || !C || (out_f32 != 0 && out_f32 != 1)) return MGEMM_ERR_INVALID_ARG;
   if (!aligned16(A) || !aligned16(Wq) || !aligned16(Ws) || !aligned16(Sw) || !aligned16(C))
     return MGEMM_ERR_INVALID_ARG;
   if (int rc = check_mnk(M, N, K)) return rc;
+  const size_t need = mg::w4a16_dec_workspace_bytes(M, N, K);
+  if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return MGEMM_ERR_WORKSPACE;
   if (int rc = check_path(MGEMM_FMT_NVFP4, MGEMM_FMT_BF16)) return rc;
   mg::Bf16Args p{(const uint16_t *)A, Wq, (const uint8_t *)Ws, Sw, C, (int)M, (int)N, (int)K,
                  out_f32, 1};
+  if (need > 0) return finish(mg::launch_w4a16_dec(p, ws, (hipStream_t)stream), "mgemm_w4a16");
   return finish(mg::launch_bf16(p, (hipStream_t)stream), "mgemm_w4a16");
 }
 
@@ -208,9 +212,9 @@ int mgemm_w4a8(const void *Aq, const float *a_tok, const void *Wq, const void *W
     return MGEMM_ERR_INVALID_ARG;
   if (int rc = check_mnk(M, N, K)) return rc;
   if (N > mg::w4a8_max_n()) return MGEMM_ERR_SHAPE;
-  if (int rc = check_path(MGEMM_FMT_NVFP4, MGEMM_FMT_FP8_E4M3_TOKEN)) return rc;
   const size_t need = mg::w4a8_workspace_bytes(M, N, K);
   if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return MGEMM_ERR_WORKSPACE;
+  if (int rc = check_path(MGEMM_FMT_NVFP4, MGEMM_FMT_FP8_E4M3_TOKEN)) return rc;
   mg::W4A8Args p{(const uint8_t *)Aq, a_tok, (const uint8_t *)Wq, (const uint8_t *)Ws, Sw, C,
                  (int)M, (int)N, (int)K, out_f32, need > 0 ? ws : nullptr};
   return finish(mg::launch_w4a8(p, (hipStream_t)stream), "mgemm_w4a8");
@@ -333,9 +337,11 @@ size_t mgemm_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int64_t T,
                              int64_t I, int64_t E, int64_t topk) {
   switch (op) {
     case MGEMM_OP_BF16:
-    case MGEMM_OP_W4A16:
     case MGEMM_OP_W4A4:
       return 0;
+    case MGEMM_OP_W4A16:
+      if (check_mnk(M, N, K) != MGEMM_OK) return 0;
+      return mg::w4a16_dec_workspace_bytes(M, N, K);
     case MGEMM_OP_W4A8:
       if (check_mnk(M, N, K) != MGEMM_OK) return 0;
       return mg::w4a8_workspace_bytes(M, N, K);

@@ -30,6 +30,10 @@ struct Bf16Args {
   int w_nvfp4;
 };
 hipError_t launch_bf16(const Bf16Args &p, hipStream_t stream);
+// small-M W4A16 (gemm_w4a16_dec.hip): split-K partials in the workspace
+constexpr int64_t W4A16_DEC_MAX_M = 128;
+size_t w4a16_dec_workspace_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_w4a16_dec(const Bf16Args &p, void *ws, hipStream_t stream);
 // backward of y = x . W^T (grad_bf16.hip): operands transposed into the
 // workspace, then the TN kernel
 size_t bf16_grad_workspace_bytes(bool wgrad, int64_t M, int64_t N, int64_t K);

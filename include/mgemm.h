@@ -133,9 +133,19 @@ int mgemm_bf16(const void *A, const void *W, void *C, int64_t M, int64_t N,
    Ws [N,K/16], Sw device float*).  Each weight element e2m1*e4m3 is widened
    to BF16 in registers (exact: at most 6 significant bits) and run on the
    BF16 MFMA; Sw is applied in the epilogue (hardware::exec docs, module
-   description: BF16 activations take the BF16 MMA with the weight widened). */
+   description: BF16 activations take the BF16 MMA with the weight widened).
+   Up to 128 tokens take a decode kernel that streams the weight once per 64
+   tokens and splits K over workgroups: each writes FP32 partial sums to
+   `ws`, and a second kernel adds them in split order (results are
+   run-to-run bit-identical).  `ws` is device memory of at least
+   mgemm_workspace_bytes(MGEMM_OP_W4A16, M, N, K, ...) bytes, 16-byte
+   aligned, with no required contents; more tokens take the tiled kernel and
+   need none (size 0: ws may be NULL).  Calls that share a workspace must be
+   ordered on one stream.  MGEMM_ERR_WORKSPACE when ws is missing, too small
+   or misaligned. */
 int mgemm_w4a16(const void *A, const void *Wq, const void *Ws, const float *Sw,
-                void *C, int64_t M, int64_t N, int64_t K, int out_f32, void *stream);
+                void *C, int64_t M, int64_t N, int64_t K, int out_f32, void *ws,
+                size_t ws_bytes, void *stream);
 
 /* W4A8: FP8 E4M3 activations Aq [M,K] with per-token FP32 scales a_tok [M]
    under NVFP4 weights.  Exact E4M3 route (hardware::exec docs, exec_of):

@@ -95,6 +95,11 @@ def test_status_strings(lib):
 def test_workspace_sizes(lib):
     assert mg.mgemm_workspace_bytes(mg.OP_BF16, 4096, 5376, 14336) == 0
     assert mg.mgemm_workspace_bytes(mg.OP_W4A4, 8192, 5376, 14336) == 0
+    # W4A16: the split-K partials (14 splits of 1024 up to 16 tokens, 28 of
+    # 512 above; 64 rows at a time) through 128 tokens, nothing above
+    for M, ks in ((1, 14), (16, 14), (17, 28), (64, 28), (128, 28)):
+        assert mg.mgemm_workspace_bytes(mg.OP_W4A16, M, 5376, 14336) == ks * min(M, 64) * 5376 * 4
+    assert mg.mgemm_workspace_bytes(mg.OP_W4A16, 129, 5376, 14336) == 0
     for M in (1, 8, 32, 128):
         assert mg.mgemm_workspace_bytes(mg.OP_W4A8, M, 5376, 14336) > 5376 * 4 * M
     moe = mg.mgemm_workspace_bytes(mg.OP_MOE, T=4096, H=4096, I=1536, E=64, topk=8)
@@ -117,7 +122,10 @@ def test_host_side_argument_errors(lib):
     assert lib.mgemm_w4a4(p, p, p, p, p, p, p, 32, 32, 32, 2, None) == -1   # bad out flag
     assert lib.mgemm_bf16(p, p, None, 32, 32, 32, 0, None) == -1
     assert lib.mgemm_bf16(p, p, p, 32, -1, 32, 0, None) == -2
-    assert lib.mgemm_w4a16(p, p, p, p, p, 32, 32, 16, 0, None) == -2
+    assert lib.mgemm_w4a16(p, p, p, p, p, 32, 32, 16, 0, p, 0, None) == -2
+    assert lib.mgemm_w4a16(p, p, p, p, p, 8, 32, 32, 0, None, 0, None) == -4   # no workspace
+    assert lib.mgemm_w4a16(p, p, p, p, p, 8, 32, 32, 0, p + 8, 1 << 20, None) == -4  # misaligned
+    assert lib.mgemm_w4a16(p, p, p, p, p, 8, 32, 32, 0, p, 16, None) == -4   # too small
     assert lib.mgemm_w4a8(p, p, p, p, p, p, 8, 32, 0, 0, p, 0, None) == -2
     assert lib.mgemm_w4a8(p, None, p, p, p, p, 8, 32, 32, 0, p, 0, None) == -1
     assert lib.mgemm_w4a8(p, p, p, p, p, p, 8, (1 << 30) + 128, 14336, 0, p, 1 << 40, None) == -2

@@ -253,7 +253,7 @@ def test_plan_on_device():
         A = torch.zeros((32, 32), dtype=torch.uint8, device="cuda")
         mg.load().mgemm_bf16  # exists
         rc = mg.load().mgemm_w4a16(A.data_ptr(), A.data_ptr(), A.data_ptr(), A.data_ptr(),
-                                   A.data_ptr(), 32, 32, 33, 0, None)
+                                   A.data_ptr(), 32, 32, 33, 0, None, 0, None)
         mg._check("mgemm_w4a16", rc)
     assert ei.value.status == -2
 
