@@ -67,7 +67,7 @@ def load() -> C.CDLL:
         "mgemm_plan": (i32, [i32, i32, i32, C.POINTER(_Plan)]),
         "mgemm_plan_arch": (i32, [C.c_char_p, i32, i32, C.POINTER(_Plan)]),
         "mgemm_pair_name": (i32, [i32, i32, C.c_char_p, C.c_size_t]),
-        "mgemm_bf16": (i32, [vp, vp, vp, i64, i64, i64, i32, vp]),
+        "mgemm_bf16": (i32, [vp, vp, vp, i64, i64, i64, i32, vp, C.c_size_t, vp]),
         "mgemm_w4a16": (i32, [vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, C.c_size_t, vp]),
         "mgemm_w4a8": (i32, [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, C.c_size_t, vp]),
         "mgemm_w4a8_noalloc": (i32, [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]),
@@ -171,14 +171,22 @@ def mgemm_workspace_bytes(op: int, M=0, N=0, K=0, T=0, H=0, I=0, E=0, topk=0) ->
 
 
 # --------------------------------------------------------------------- GEMMs
-def mgemm_bf16(A: torch.Tensor, W: torch.Tensor, C_out: torch.Tensor, stream=None) -> torch.Tensor:
+def mgemm_bf16(A: torch.Tensor, W: torch.Tensor, C_out: torch.Tensor,
+               ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     M, K = A.shape
     N = W.shape[0]
     _need(A, "A", _BF16_T, (M, K))
     _need(W, "W", _BF16_T, (N, K))
     _need(C_out, "C", _C_T, (M, N))
+    need = mgemm_workspace_bytes(OP_BF16, M, N, K)
+    if ws is None:
+        ws = workspace(need, "bf16", stream)
+    if need and (ws is None or ws.numel() * ws.element_size() < need):
+        raise ValueError("bf16: workspace too small")
+    wp = ws.data_ptr() if ws is not None else None
+    wb = ws.numel() * ws.element_size() if ws is not None else 0
     _check("mgemm_bf16", load().mgemm_bf16(A.data_ptr(), W.data_ptr(), C_out.data_ptr(), M, N, K,
-                                           _out_f32(C_out), _stream(stream)))
+                                           _out_f32(C_out), wp, wb, _stream(stream)))
     return C_out
 
 

@@ -177,13 +177,15 @@ int mgemm_pair_name(int w_fmt, int a_fmt, char *buf, size_t len) {
 }
 
 int mgemm_bf16(const void *A, const void *W, void *C, int64_t M, int64_t N, int64_t K,
-               int out_f32, void *stream) {
+               int out_f32, void *ws, size_t ws_bytes, void *stream) {
   if (!A || !W || !C || (out_f32 != 0 && out_f32 != 1)) return MGEMM_ERR_INVALID_ARG;
   if (!aligned16(A) || !aligned16(W) || !aligned16(C)) return MGEMM_ERR_INVALID_ARG;
   if (int rc = check_mnk(M, N, K)) return rc;
   if (int rc = check_path(MGEMM_FMT_BF16, MGEMM_FMT_BF16)) return rc;
+  const size_t need = mg::bf16_workspace_bytes(M, N, K);
+  if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return MGEMM_ERR_WORKSPACE;
   mg::Bf16Args p{(const uint16_t *)A, W, nullptr, nullptr, C, (int)M, (int)N, (int)K, out_f32, 0};
-  return finish(mg::launch_bf16(p, (hipStream_t)stream), "mgemm_bf16");
+  return finish(mg::launch_bf16(p, need > 0 ? ws : nullptr, (hipStream_t)stream), "mgemm_bf16");
 }
 
 int mgemm_w4a16(const void *A, const void *Wq, const void *Ws, const float *Sw, void *C,
@@ -199,7 +201,7 @@ int mgemm_w4a16(const void *A, const void *Wq, const void *Ws, const float *Sw, 
   mg::Bf16Args p{(const uint16_t *)A, Wq, (const uint8_t *)Ws, Sw, C, (int)M, (int)N, (int)K,
                  out_f32, 1};
   if (need > 0) return finish(mg::launch_w4a16_dec(p, ws, (hipStream_t)stream), "mgemm_w4a16");
-  return finish(mg::launch_bf16(p, (hipStream_t)stream), "mgemm_w4a16");
+  return finish(mg::launch_bf16(p, nullptr, (hipStream_t)stream), "mgemm_w4a16");
 }
 
 int mgemm_w4a8(const void *Aq, const float *a_tok, const void *Wq, const void *Ws,
@@ -336,9 +338,11 @@ int mgemm_moe_route_topk(const float *logits, int64_t T, int64_t E, int64_t topk
 size_t mgemm_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int64_t T, int64_t H,
                              int64_t I, int64_t E, int64_t topk) {
   switch (op) {
-    case MGEMM_OP_BF16:
     case MGEMM_OP_W4A4:
       return 0;
+    case MGEMM_OP_BF16:
+      if (check_mnk(M, N, K) != MGEMM_OK) return 0;
+      return mg::bf16_workspace_bytes(M, N, K);
     case MGEMM_OP_W4A16:
       if (check_mnk(M, N, K) != MGEMM_OK) return 0;
       return mg::w4a16_dec_workspace_bytes(M, N, K);

@@ -160,6 +160,15 @@ __device__ __forceinline__ void dma16(const void *g, const void *lds) {
                "s"(lds_addr(lds))
                : "memory", "m0");
 }
+// the same load addressed as a uniform 64-bit base plus a 32-bit per-lane
+// byte offset: the offsets of a tile's rows stay fixed from stage to stage
+// (only the base moves along K), so they cost one register each
+// (lds: the LDS byte address, uniform)
+__device__ __forceinline__ void dma16_s(uint32_t off, const void *base, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off),
+               "s"(base), "s"(lds)
+               : "memory", "m0");
+}
 __device__ __forceinline__ void dma2(const void *g, const void *lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_ushort %0, off" ::"v"(g),
                "s"(lds_addr(lds))

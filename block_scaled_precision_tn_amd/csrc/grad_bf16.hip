@@ -58,9 +58,11 @@ size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
+// transposed operands, then the TN product's tail partials (bf16_workspace_bytes)
 size_t bf16_grad_workspace_bytes(bool wgrad, int64_t M, int64_t N, int64_t K) {
-  if (!wgrad) return up256((size_t)N * (size_t)K * 2);
-  return up256((size_t)M * (size_t)N * 2) + up256((size_t)M * (size_t)K * 2);
+  if (!wgrad) return up256((size_t)N * (size_t)K * 2) + bf16_workspace_bytes(M, K, N);
+  return up256((size_t)M * (size_t)N * 2) + up256((size_t)M * (size_t)K * 2) +
+         bf16_workspace_bytes(N, K, M);
 }
 
 hipError_t launch_bf16_dgrad(const uint16_t *dY, const uint16_t *W, void *dX, int M, int N, int K,
@@ -69,7 +71,7 @@ hipError_t launch_bf16_dgrad(const uint16_t *dY, const uint16_t *W, void *dX, in
   hipError_t e = transpose(W, wt, N, K, stream);
   if (e != hipSuccess) return e;
   Bf16Args p{dY, wt, nullptr, nullptr, dX, M, K, N, out_f32, 0};
-  return launch_bf16(p, stream);
+  return launch_bf16(p, (char *)ws + up256((size_t)N * (size_t)K * 2), stream);
 }
 
 hipError_t launch_bf16_wgrad(const uint16_t *dY, const uint16_t *X, void *dW, int M, int N, int K,
@@ -81,7 +83,7 @@ hipError_t launch_bf16_wgrad(const uint16_t *dY, const uint16_t *X, void *dW, in
   e = transpose(X, xt, M, K, stream);
   if (e != hipSuccess) return e;
   Bf16Args p{dyt, xt, nullptr, nullptr, dW, N, K, M, out_f32, 0};
-  return launch_bf16(p, stream);
+  return launch_bf16(p, (char *)xt + up256((size_t)M * (size_t)K * 2), stream);
 }
 
 }  // namespace mg

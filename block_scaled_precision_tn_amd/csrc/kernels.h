@@ -28,15 +28,24 @@ struct Bf16Args {
   int M, N, K;
   int out_f32;
   int w_nvfp4;
+  // BF16 x BF16 tail split (set by launch_bf16): workgroups past the first
+  // full_tiles each take one of `split` K ranges of a remaining tile and
+  // write an FP32 partial tile to part
+  int full_tiles = 0;
+  int split = 1;
+  float *part = nullptr;
 };
-hipError_t launch_bf16(const Bf16Args &p, hipStream_t stream);
+// BF16 x BF16 (w_nvfp4 = 0) may split the tiles of the grid's last, partial
+// round along K; the partials need bf16_workspace_bytes of ws
+size_t bf16_workspace_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_bf16(const Bf16Args &p, void *ws, hipStream_t stream);
 // small-M W4A16 (gemm_w4a16_dec.hip): split-K partials in the workspace
 constexpr int64_t W4A16_DEC_MAX_M = 128;
 size_t w4a16_dec_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_w4a16_dec(const Bf16Args &p, void *ws, hipStream_t stream);
 // backward of y = x . W^T (grad_bf16.hip): operands transposed into the
 // workspace, then the TN kernel
-size_t bf16_grad_workspace_bytes(bool wgrad, int64_t M, int64_t N, int64_t K);
+size_t bf16_grad_workspace_bytes(bool wgrad, int64_t M, int64_t N, int64_t K);  // transposes + tail partials
 hipError_t launch_bf16_dgrad(const uint16_t *dY, const uint16_t *W, void *dX, int M, int N, int K,
                              int out_f32, void *ws, hipStream_t stream);
 hipError_t launch_bf16_wgrad(const uint16_t *dY, const uint16_t *X, void *dW, int M, int N, int K,

@@ -125,9 +125,18 @@ int mgemm_pair_name(int w_fmt, int a_fmt, char *buf, size_t len);
 
 /* W16A16: C = A . W^T with BF16 A [M,K] and W [N,K] on the BF16 MFMA,
    FP32 accumulation (the H3 FFN down-projection of RL-Kernel PR #535:
-   BF16 MMA tiles, FP32 accumulation, BF16 epilogue). */
+   BF16 MMA tiles, FP32 accumulation, BF16 epilogue).  The grid runs one
+   256x256 tile per workgroup (256x128 when an operand reaches 4 GiB) and
+   one workgroup per CU; when the tiles fill the last round only in part,
+   those tiles are split into K ranges whose
+   FP32 partial tiles go to `ws` and a second kernel adds them in range
+   order (results are run-to-run bit-identical).  `ws`: device memory of at
+   least mgemm_workspace_bytes(MGEMM_OP_BF16, M, N, K, ...) bytes, 16-byte
+   aligned, no required contents (size 0: ws may be NULL).  Calls that share
+   a workspace must be ordered on one stream.  MGEMM_ERR_WORKSPACE when ws
+   is missing, too small or misaligned. */
 int mgemm_bf16(const void *A, const void *W, void *C, int64_t M, int64_t N,
-               int64_t K, int out_f32, void *stream);
+               int64_t K, int out_f32, void *ws, size_t ws_bytes, void *stream);
 
 /* W4A16: BF16 activations A [M,K] under NVFP4 weights (Wq [N,K/2],
    Ws [N,K/16], Sw device float*).  Each weight element e2m1*e4m3 is widened

@@ -93,7 +93,10 @@ def test_status_strings(lib):
 
 
 def test_workspace_sizes(lib):
-    assert mg.mgemm_workspace_bytes(mg.OP_BF16, 4096, 5376, 14336) == 0
+    # BF16: 336 tiles of 256x256 on 256 CUs leave a last round of 80 tiles,
+    # split 3 ways along K (FP32 partial tiles); 256 tiles fill one round
+    assert mg.mgemm_workspace_bytes(mg.OP_BF16, 4096, 5376, 14336) == 80 * 3 * 256 * 256 * 4
+    assert mg.mgemm_workspace_bytes(mg.OP_BF16, 4096, 4096, 14336) == 0
     assert mg.mgemm_workspace_bytes(mg.OP_W4A4, 8192, 5376, 14336) == 0
     # W4A16: the split-K partials (14 splits of 1024 up to 16 tokens, 28 of
     # 512 above; 64 rows at a time) through 128 tokens, nothing above
@@ -120,8 +123,8 @@ def test_host_side_argument_errors(lib):
     assert lib.mgemm_w4a4(p, p, p, p, p, p, p, 0, 32, 32, 0, None) == -2    # M = 0
     assert lib.mgemm_w4a4(p + 8, p, p, p, p, p, p, 32, 32, 32, 0, None) == -1  # misaligned
     assert lib.mgemm_w4a4(p, p, p, p, p, p, p, 32, 32, 32, 2, None) == -1   # bad out flag
-    assert lib.mgemm_bf16(p, p, None, 32, 32, 32, 0, None) == -1
-    assert lib.mgemm_bf16(p, p, p, 32, -1, 32, 0, None) == -2
+    assert lib.mgemm_bf16(p, p, None, 32, 32, 32, 0, None, 0, None) == -1
+    assert lib.mgemm_bf16(p, p, p, 32, -1, 32, 0, None, 0, None) == -2
     assert lib.mgemm_w4a16(p, p, p, p, p, 32, 32, 16, 0, p, 0, None) == -2
     assert lib.mgemm_w4a16(p, p, p, p, p, 8, 32, 32, 0, None, 0, None) == -4   # no workspace
     assert lib.mgemm_w4a16(p, p, p, p, p, 8, 32, 32, 0, p + 8, 1 << 20, None) == -4  # misaligned

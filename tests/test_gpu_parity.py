@@ -283,3 +283,45 @@ def test_w4a8_concurrent_streams_own_workspaces():
         c64, b64 = oracle_full("w4a8", inp)
         from gpu_cases import w4a8_window
         check_f32(C.cpu().numpy(), c64, b64, what="w4a8 stream", extra=w4a8_window(inp))
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 640, 2048),    # 6 tiles of 256 x 256, all split (8 ranges)
+                                   (520, 1000, 1568),   # partial K stage in the last range
+                                   (300, 652, 2048),    # N % 8 != 0: the sum's element-wise stores
+                                   (256, 384, 1024)])
+def test_bf16_tail_split(M, N, K):
+    """Grids that leave a partial last round split those tiles along K (FP32
+    partial tiles, then an ordered sum): parity with the oracle in FP32 and
+    BF16, repeat bit-identical, an explicit workspace of exactly the reported
+    size with arbitrary contents accepted, one byte less refused."""
+    import block_scaled_precision_tn_amd as mg
+    from gpu_cases import check_both, oracle_full, dev, out_tensor, to_np
+    inp = synth.bf16(M, N, K, seed=M + N)
+    c64, b64 = oracle_full("bf16", inp)
+    check_both("bf16", inp, c64, b64, what=f"bf16 split {M}x{N}x{K}")
+    need = mg.mgemm_workspace_bytes(mg.OP_BF16, M, N, K)
+    assert need > 0
+    A = dev(inp["a"].view(np.int16), torch.bfloat16)
+    W = dev(inp["w"].view(np.int16), torch.bfloat16)
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda")
+    outs = []
+    for _ in range(2):
+        C = out_tensor(M, N, True)
+        mg.mgemm_bf16(A, W, C, ws=ws)
+        torch.cuda.synchronize()
+        outs.append(to_np(C))
+    check_f32(outs[0], c64, b64)
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+    with pytest.raises(ValueError):
+        mg.mgemm_bf16(A, W, out_tensor(M, N, True), ws=ws[:need - 1])
+
+
+@pytest.mark.parametrize("M,N,K", [(4000, 4000, 96),    # 256 ragged tiles: one whole round
+                                   (4000, 4100, 512)])  # 272 tiles: 256 whole, 16 split in 2
+def test_bf16_whole_tiles(M, N, K):
+    """Grids of at least one tile per CU: whole tiles (the partial K stage
+    included) next to split ones, every output against the oracle."""
+    from gpu_cases import check_both, oracle_full
+    inp = synth.bf16(M, N, K, seed=M + K)
+    c64, b64 = oracle_full("bf16", inp)
+    check_both("bf16", inp, c64, b64, what=f"bf16 whole tiles {M}x{N}x{K}")
