@@ -13,8 +13,8 @@
 // Stream-ordered kernels:
 //   k_prep   zero the expert counters
 //   k_count  per-expert histogram; each entry's rank within its expert
-//   k_scan   expert row offsets and the 128-row tile list (so the grouped
-//            GEMM grids need no host sync)
+//   k_scan   expert row offsets and the tile list (128 or 256 rows per
+//            tile; the grouped GEMM grids need no host sync)
 //   k_scatter each entry's sorted row (entries grouped by expert)
 //   k_gateup grouped GEMM on the E8M0-scaled FP8 MFMA with gathered token
 //            rows; epilogue: GLU, MXFP8 re-quantisation of h (block amax by
@@ -97,6 +97,7 @@ __global__ __launch_bounds__(1024) void k_count(const int32_t *ids, int R, int E
 
 // one workgroup: exclusive scans of the expert counts (row offsets) and of
 // their tile counts (tile list: expert, first row, rows)
+template <int TM>
 __global__ __launch_bounds__(256) void k_scan(const uint32_t *counts, int E, int32_t *offs,
                                               int32_t *meta, int32_t *tile_e, int32_t *tile_r,
                                               int32_t *tile_n) {
@@ -109,7 +110,7 @@ __global__ __launch_bounds__(256) void k_scan(const uint32_t *counts, int E, int
     const int e = tid * PER + k;
     const int c = e < E ? (int)counts[CSTRIDE * e] : 0;
     rows[k] = c;
-    tiles[k] = (c + BM - 1) / BM;
+    tiles[k] = (c + TM - 1) / TM;
     r += c;
     t += tiles[k];
   }
@@ -132,8 +133,8 @@ __global__ __launch_bounds__(256) void k_scan(const uint32_t *counts, int E, int
       offs[e] = rb;
       for (int q = 0; q < tiles[k]; ++q) {
         tile_e[tb + q] = e;
-        tile_r[tb + q] = rb + q * BM;
-        tile_n[tb + q] = rows[k] - q * BM < BM ? rows[k] - q * BM : BM;
+        tile_r[tb + q] = rb + q * TM;
+        tile_n[tb + q] = rows[k] - q * TM < TM ? rows[k] - q * TM : TM;
       }
     }
     rb += rows[k];
@@ -357,11 +358,26 @@ __device__ __forceinline__ void mx_mainloop(const MxRows &rows, int Ktot, const 
     mx_mainloop_sc2<NB>(rows, Ktot, bsel, acc);
 }
 
+// max over the 32 lanes that share (lane / 32): within each row of 16 lanes
+// by DPP on the vector ALU (the other lane of the pair, of the quad's pair,
+// the mirror lane of the half row, of the row), then one lane exchange with
+// the other row of the 32
+__device__ __forceinline__ float dpp_max(float v, int ctrl_kind) {
+  int o;
+  switch (ctrl_kind) {
+    case 0: o = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false); break;   // quad_perm [1,0,3,2]
+    case 1: o = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false); break;   // quad_perm [2,3,0,1]
+    case 2: o = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false); break;  // row_half_mirror
+    default: o = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false); break; // row_mirror
+  }
+  return fmaxf(v, __builtin_bit_cast(float, o));
+}
 __device__ __forceinline__ float max32_lanes(float v) {
-  // max over the 32 lanes that share (lane / 32)
-#pragma unroll
-  for (int o = 1; o < 32; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  v = dpp_max(v, 0);
+  v = dpp_max(v, 1);
+  v = dpp_max(v, 2);
+  v = dpp_max(v, 3);
+  return fmaxf(v, __shfl_xor(v, 16, 64));
 }
 
 template <bool SC16>
@@ -501,6 +517,259 @@ __global__ __launch_bounds__(256) void k_down(MoeArgs p, const int32_t *meta, co
       }
     }
 }
+
+// ----------------------------------- grouped GEMMs on 256 x 256 tiles
+// For the large calls (H and I multiples of 512) both grouped GEMMs run on
+// 256-row tiles of routed rows (the tile list is built for 256 rows) against
+// 256 weight rows: gate/up takes 128 gate and the 128 matching up rows (128
+// h columns), down 256 hidden columns.  Eight waves (4 x 2) each compute
+// 64 x 128 (2 x 4 blocks of 32 x 32 on the E8M0-scaled 32x32x64 FP8 MFMA),
+// so a wave reads 6 operand fragments per 8 MFMAs (a 64 x 64 wave tile
+// reads 4 per 4).  K is staged 128 bytes per row (8 rows x 128 bytes per
+// load instruction: whole cache lines) through two 64 KiB LDS slots: stage
+// s+2 is requested right after the barrier that follows the last read of
+// stage s.  Rows are XOR-swizzled in 16-byte chunks as in the BF16 kernel.
+// A lane's row offsets are fixed for the tile (gathered rows included) and
+// stay in registers; only the operand base moves along K.  Each row's E8M0
+// scale bytes arrive 16 at a time (four stages) straight into a
+// double-buffered LDS chunk.  Within a K-step the B fragments are read one
+// block column ahead of the MFMAs that use them.  A wave whose 64 rows all
+// lie past the tile's routed rows skips its MFMAs.
+namespace t2 {
+
+constexpr int TM = 256, TN = 256, TK = 128;   // routed rows, weight rows, K bytes per stage
+constexpr int NT = 512;
+constexpr int STG = TM * TK;                  // bytes of one operand's codes per stage
+constexpr int CHK = 4;                        // stages per scale chunk (16 bytes per row)
+
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return row * TK + ((chunk ^ ((row >> 1) & 7)) << 4);
+}
+// lane's j-th load of a stage (j < 4): row 8 (4 wave + j) + lane / 8, its
+// LDS slot lane % 8 holds global chunk slot ^ ((row / 2) % 8)
+__device__ __forceinline__ int ld_row(int wave, int j, int lane) { return 8 * (4 * wave + j) + (lane >> 3); }
+__device__ __forceinline__ int ld_chunk(int row, int lane) { return (lane & 7) ^ ((row >> 1) & 7); }
+
+__device__ __forceinline__ void issue(const uint8_t *base, int k0, const uint32_t (&off)[4],
+                                      uint32_t lds, int wave) {
+  const uint8_t *b = base + k0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) dma16_s(off[j], b, lds + 1024u * (4 * wave + j));
+}
+
+template <int OPSEL>
+__device__ __forceinline__ f32x16 mfma_mx(i32x8 a, i32x8 b, f32x16 c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, OPSEL, sa, OPSEL, sb);
+}
+
+template <bool GU>
+__global__ __launch_bounds__(NT, 1) void k_mx256(MoeArgs p, const int32_t *meta,
+                                                 const int32_t *sorted, const float *wsorted,
+                                                 const int32_t *tile_e, const int32_t *tile_r,
+                                                 const int32_t *tile_n, uint8_t *hq, uint8_t *hs,
+                                                 float *y) {
+  __shared__ __attribute__((aligned(1024))) uint8_t la0[STG], la1[STG], lb0[STG], lb1[STG];
+  __shared__ __attribute__((aligned(16))) uint8_t scs[2][2 * TM * 16];   // [chunk & 1][row][16]
+  __shared__ float s_w[TM];
+
+  const int tile = blockIdx.y;
+  if (tile >= meta[0]) return;
+  const int e = tile_e[tile], r0 = tile_r[tile], nrows = tile_n[tile];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1, h = lane >> 5, l32 = lane & 31;
+  const int H = p.H, I = p.I;
+  const int K = GU ? H : I;
+  const int c0 = blockIdx.x * (GU ? TN / 2 : TN);   // first h column / hidden column
+
+  // A: gathered token rows (gate/up) or sorted h rows (down); rows past the
+  // tile read its first row (never stored).  B: gate rows c0.., then up rows
+  // I + c0.. (gate/up), or w2 rows c0.. clamped to H (down).
+  const uint8_t *abase = GU ? p.xq : hq;
+  const uint8_t *bbase = GU ? p.w13q + (int64_t)e * 2 * I * H : p.w2q + (int64_t)e * H * I;
+  auto a_row = [&](int row) -> int {
+    const int rr = row < nrows ? row : 0;
+    return GU ? sorted[r0 + rr] / p.topk : r0 + rr;
+  };
+  auto b_row = [&](int row) -> int {
+    if (GU) return row < TN / 2 ? c0 + row : I + c0 + (row - TN / 2);
+    return c0 + row < H ? c0 + row : H - 1;
+  };
+  uint32_t offa[4], offb[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = ld_row(wave, j, lane), ch = ld_chunk(row, lane);
+    offa[j] = (uint32_t)a_row(row) * (uint32_t)K + 16u * ch;
+    offb[j] = (uint32_t)b_row(row) * (uint32_t)K + 16u * ch;
+  }
+  // this thread's scale row: A row tid (< 256) or B row tid - 256
+  const uint8_t *srow;
+  if (tid < TM)
+    srow = (GU ? p.xs : hs) + (int64_t)a_row(tid) * (K / 32);
+  else
+    srow = (GU ? p.w13s + (int64_t)e * 2 * I * (H / 32) : p.w2s + (int64_t)e * H * (I / 32)) +
+           (int64_t)b_row(tid - TM) * (K / 32);
+  float wrow = 0.0f;
+  if (!GU && tid < TM) wrow = wsorted[r0 + (tid < nrows ? tid : 0)];
+
+  const int S = K / TK, NCH = S / CHK;
+  const bool act = wm * 64 < nrows;   // this wave's rows exist
+  int bsel[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    bsel[j] = GU ? (j < 2 ? wn * 64 + 32 * j : TN / 2 + wn * 64 + 32 * (j - 2)) : wn * 128 + 32 * j;
+
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{0};
+
+  // scale chunk c (16 bytes of every row) goes straight to scs[c & 1]: lane
+  // i of wave w lands at 16 (64 w + i), the thread's own row
+  dma16(srow, scs[0] + 1024 * wave);
+  issue(abase, 0, offa, lds_addr(la0), wave);
+  issue(bbase, 0, offb, lds_addr(lb0), wave);
+  issue(abase, (1 < S ? 1 : 0) * TK, offa, lds_addr(la1), wave);
+  issue(bbase, (1 < S ? 1 : 0) * TK, offb, lds_addr(lb1), wave);
+
+  // the stage's scale dwords (bytes of this lane's block in 0 and 2)
+  int sa[2], sb[4];
+  auto scales = [&](int s) {
+    const uint8_t *c = scs[(s / CHK) & 1] + 4 * (s % CHK);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) sa[i] = (int)(*(const uint32_t *)(c + 16 * (wm * 64 + 32 * i + l32)) >> (8 * h));
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      sb[j] = (int)(*(const uint32_t *)(c + 16 * (TM + bsel[j] + l32)) >> (8 * h));
+  };
+  // operand fragment of tile row `row` for K-step kk: 16-byte chunks 4 kk + h
+  // and 4 kk + 2 + h (the MFMA's two 32-element scale blocks)
+  auto frag = [&](const uint8_t *l, int row, int kk) {
+    const u32x4 lo = *(const u32x4 *)(l + swz(row, 4 * kk + h));
+    const u32x4 hi = *(const u32x4 *)(l + swz(row, 4 * kk + 2 + h));
+    return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  };
+  // one K-step: the two A fragments, then the B fragments one block column
+  // ahead of the MFMAs that use them, so LDS reads and MFMAs interleave
+  auto kstep = [&](const uint8_t *la, const uint8_t *lb, int kk) {
+    i32x8 fa[2], fb[2];
+    fa[0] = frag(la, wm * 64 + l32, kk);
+    fa[1] = frag(la, wm * 64 + 32 + l32, kk);
+    fb[0] = frag(lb, bsel[0] + l32, kk);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (j + 1 < 4) fb[(j + 1) & 1] = frag(lb, bsel[j + 1] + l32, kk);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        acc[i][j] = kk == 0 ? mfma_mx<0>(fa[i], fb[j & 1], acc[i][j], sa[i], sb[j])
+                            : mfma_mx<2>(fa[i], fb[j & 1], acc[i][j], sa[i], sb[j]);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // fa[0], fa[1], fb[0], fb[1]
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      if (j + 2 < 4) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+  };
+  // stage s: slot (la, lb) readable (loads landed, every wave past the barrier)
+  auto ready = [&]() {
+    wait_vmcnt<0>();
+    wait_lgkm0();
+    __builtin_amdgcn_s_barrier();
+  };
+  // stage s computed from (la, lb); stage s+1 waits in (na, nb): after the
+  // barrier that follows the stage's last reads, stage s+2 goes to (la, lb)
+  auto step = [&](int s, uint8_t *la, uint8_t *lb, uint8_t *na, uint8_t *nb) {
+    __builtin_amdgcn_sched_barrier(0);
+    // the next chunk's scales go to the buffer chunk s/CHK - 1 used (every
+    // wave is past its last read); they land before this stage ends
+    if (s % CHK == 0 && s / CHK + 1 < NCH)
+      dma16(srow + 16 * (s / CHK + 1), scs[(s / CHK + 1) & 1] + 1024 * wave);
+    if (act) {
+      scales(s);
+      __builtin_amdgcn_sched_barrier(0);
+      kstep(la, lb, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      kstep(la, lb, 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (s + 1 < S) {
+      ready();
+      const int t = s + 2 < S ? s + 2 : S - 1;
+      issue(abase, t * TK, offa, lds_addr(la), wave);
+      issue(bbase, t * TK, offb, lds_addr(lb), wave);
+    }
+  };
+  ready();
+  for (int s = 0; s < S; s += 2) {
+    step(s, la0, lb0, la1, lb1);
+    if (s + 1 < S) step(s + 1, la1, lb1, la0, lb0);
+  }
+  wait_vmcnt<0>();
+
+  if constexpr (GU) {
+    // h = silu(g) * u; the MXFP8 block of 32 h columns is a wave's 32 lanes
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int col = c0 + wn * 64 + 32 * jj + l32;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = wm * 64 + i * 32 + acc_row(r, lane);
+          const float g = acc[i][jj][r], u = acc[i][jj + 2][r];
+          const float hv = (g / (1.0f + expf(-g))) * u;
+          const float amax = max32_lanes(fabsf(hv));
+          uint32_t sbyte, code;
+          if (amax == 0.0f) {
+            sbyte = 0u;
+            code = 0u;
+          } else {
+            int X = (int)((__builtin_bit_cast(uint32_t, amax) >> 23) & 0xFF) - 127 - 8;
+            X = X < -127 ? -127 : (X > 127 ? 127 : X);
+            sbyte = (uint32_t)(X + 127);
+            code = f32_to_e4m3_rne_sat(__builtin_ldexpf(hv, -X));
+          }
+          if (row < nrows) {
+            const int64_t srow2 = r0 + row;
+            if (p.dbg_gu) {
+              float *d = p.dbg_gu + (int64_t)sorted[srow2] * (2 * I);
+              d[col] = g;
+              d[I + col] = u;
+            }
+            hq[srow2 * I + col] = (uint8_t)code;
+            if (l32 == 0) hs[srow2 * (I / 32) + col / 32] = (uint8_t)sbyte;
+            if (p.dbg_h) {
+              const int64_t ent = sorted[srow2];
+              uint8_t *d = p.dbg_h + ent * (int64_t)(I + I / 32);
+              d[col] = (uint8_t)code;
+              if (l32 == 0) d[I + col / 32] = (uint8_t)sbyte;
+            }
+          }
+        }
+    }
+  } else {
+    if (tid < TM) s_w[tid] = wrow;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = wm * 64 + i * 32 + acc_row(r, lane);
+        if (row >= nrows) continue;
+        const float w = s_w[row];
+        float *yrow = y + (int64_t)(r0 + row) * H;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int n = c0 + wn * 128 + 32 * j + l32;
+          if (n < H) yrow[n] = acc[i][j][r] * w;
+        }
+      }
+  }
+}
+
+}  // namespace t2
 
 // ------------------------------------------- decode-sized MoE (swap-AB)
 // With few tokens each expert holds at most a few routed rows, and the call
@@ -942,6 +1211,15 @@ __global__ __launch_bounds__(1024) void k_route_small(const int32_t *ids, const 
 // the decode-sized kernels serve up to 32 tokens when both K dimensions are
 // whole stages (an expert then has at most 32 rows unless a token names it
 // twice; such rows are taken 32 at a time)
+// the 256 x 256 grouped GEMMs: scale rows in 16-byte chunks (H, I multiples
+// of 512), 128 h columns per gate/up tile, and every row offset of an
+// operand within 32 bits
+static bool mx256_path(const MoeArgs &p) {
+  const int64_t R = (int64_t)p.T * p.topk, lim = (int64_t)1 << 32;
+  return p.H % 512 == 0 && p.I % 512 == 0 && (int64_t)p.T * p.H < lim && R * p.I < lim &&
+         (int64_t)2 * p.I * p.H < lim;
+}
+
 static bool dec_path(const MoeArgs &p) {
   return p.T <= 32 && (int64_t)p.T * p.topk <= 1024 && p.H % DKS == 0 && p.I % DKS == 0;
 }
@@ -1026,10 +1304,25 @@ hipError_t launch_moe(const MoeArgs &p, hipStream_t stream) {
       hipLaunchKernelGGL(k_count_logits<16>, gr, dim3(1024), 0, stream, p.logits, p.T, p.E, p.topk,
                          ids, tw, counts, pos);
   }
-  hipLaunchKernelGGL(k_scan, dim3(1), dim3(256), 0, stream, counts, p.E, offs, meta, tile_e,
-                     tile_r, tile_n);
+  const bool big = mx256_path(p);
+  if (big)
+    hipLaunchKernelGGL(k_scan<t2::TM>, dim3(1), dim3(256), 0, stream, counts, p.E, offs, meta,
+                       tile_e, tile_r, tile_n);
+  else
+    hipLaunchKernelGGL(k_scan<BM>, dim3(1), dim3(256), 0, stream, counts, p.E, offs, meta, tile_e,
+                       tile_r, tile_n);
   hipLaunchKernelGGL(k_scatter, dim3(rb), dim3(256), 0, stream, p.ids, p.tw, L.R, offs, pos, sorted,
                      wsorted);
+  if (big) {
+    const dim3 g2(p.I / (t2::TN / 2), L.maxtiles), d2((p.H + t2::TN - 1) / t2::TN, L.maxtiles);
+    hipLaunchKernelGGL(t2::k_mx256<true>, g2, dim3(t2::NT), 0, stream, p, meta, sorted, wsorted,
+                       tile_e, tile_r, tile_n, hq, hs, y);
+    hipLaunchKernelGGL(t2::k_mx256<false>, d2, dim3(t2::NT), 0, stream, p, meta, sorted, wsorted,
+                       tile_e, tile_r, tile_n, hq, hs, y);
+    hipLaunchKernelGGL(k_combine, dim3((unsigned)((TH4 + 255) / 256)), dim3(256), 0, stream, y,
+                       pos, p.T, p.H, p.topk, p.out);
+    return hipGetLastError();
+  }
   // scale rows of 16-byte multiples (K % 512 == 0) take the chunked scale loads
   const dim3 gg(p.I / BNI, L.maxtiles), gd((p.H + BNH - 1) / BNH, L.maxtiles);
   if (p.H % 512 == 0)
@@ -1084,7 +1377,7 @@ hipError_t launch_moe4(const Moe4Args &p, hipStream_t stream) {
     hipLaunchKernelGGL(k_prep, dim3((p.E + 255) / 256), dim3(256), 0, stream, counts, p.E);
     hipLaunchKernelGGL(k_count, dim3((L.R + 1023) / 1024), dim3(1024), 0, stream, p.ids, L.R,
                        p.E, counts, pos);
-    hipLaunchKernelGGL(k_scan, dim3(1), dim3(256), 0, stream, counts, p.E, offs, meta, tile_e,
+    hipLaunchKernelGGL(k_scan<BM>, dim3(1), dim3(256), 0, stream, counts, p.E, offs, meta, tile_e,
                        tile_r, tile_n);
     hipLaunchKernelGGL(k_scatter, dim3(rb), dim3(256), 0, stream, p.ids, p.tw, L.R, offs, pos,
                        sorted, wsorted);

@@ -183,12 +183,15 @@ def _check_down_combine(inp, d, out, T, H, I, topk, tokens):
     check_bf16_vs(out[tokens], ref, bnd, what="moe out", extra=extra)
 
 
-# More than 32 tokens take the grouped kernels: H or I a multiple of 512
-# takes the chunked scale loads (16 bytes of a scale row per lane for 8
-# stages), the others the per-stage 2-byte loads.  Up to 32 tokens with H and
-# I multiples of 128 take the decode-sized (swap-AB) kernels.
+# More than 32 tokens take the grouped kernels: with H and I multiples of 512
+# the 256 x 256 tiles (tile list of 256 rows), otherwise 128 x 128 tiles,
+# where H or I a multiple of 512 takes the chunked scale loads (16 bytes of a
+# scale row per lane for 8 stages) and the others the per-stage 2-byte
+# loads.  Up to 32 tokens with H and I multiples of 128 take the
+# decode-sized (swap-AB) kernels.
 @pytest.mark.parametrize("T,H,I,E,topk", [(64, 256, 128, 8, 4), (300, 128, 192, 6, 3),
                                           (33, 64, 64, 16, 2), (40, 1024, 512, 4, 2),
+                                          (300, 512, 512, 4, 2), (160, 512, 1024, 8, 2),
                                           (24, 512, 1536, 3, 2), (1, 512, 256, 8, 4),
                                           (7, 256, 384, 16, 3), (32, 1024, 512, 8, 2),
                                           (16, 128, 128, 64, 8), (5, 64, 128, 4, 2)])
@@ -211,6 +214,22 @@ def test_moe_skewed_routing_and_empty_experts():
     ids[:, 1] = np.where(ids[:, 1] == ids[:, 0], (ids[:, 0] + 1) % 4, ids[:, 1])
     inp["ids"] = ids
     out, d = run_moe(inp, T, H, I, E, topk)
+    _check_requant(inp, d, T, H, I, topk)
+    _check_down_combine(inp, d, out, T, H, I, topk, np.arange(T))
+
+
+def test_moe_skewed_routing_big_tiles():
+    """The 256-row tiles: one expert holds a full tile and a partial one,
+    another one partial tile, the rest 1 to 35 rows (tiles whose idle waves
+    skip their MFMAs) or none."""
+    T, H, I, E, topk = 300, 512, 512, 8, 2
+    inp = synth.moe(T, H, I, E, topk, seed=6)
+    rng = np.random.default_rng(6)
+    ids = np.where(rng.random((T, topk)) < 0.85, 3, rng.integers(0, 3, (T, topk))).astype(np.int32)
+    ids[:, 1] = np.where(ids[:, 1] == ids[:, 0], (ids[:, 0] + 5) % E, ids[:, 1])
+    inp["ids"] = ids
+    out, d, gu = run_moe(inp, T, H, I, E, topk, gu=True)
+    _check_gateup(inp, gu, T, H, I, topk)
     _check_requant(inp, d, T, H, I, topk)
     _check_down_combine(inp, d, out, T, H, I, topk, np.arange(T))
 
