@@ -372,11 +372,14 @@ __device__ __forceinline__ float dpp_max(float v, int ctrl_kind) {
   }
   return fmaxf(v, __builtin_bit_cast(float, o));
 }
-__device__ __forceinline__ float max32_lanes(float v) {
+__device__ __forceinline__ float row_max16(float v) {
   v = dpp_max(v, 0);
   v = dpp_max(v, 1);
   v = dpp_max(v, 2);
-  v = dpp_max(v, 3);
+  return dpp_max(v, 3);
+}
+__device__ __forceinline__ float max32_lanes(float v) {
+  v = row_max16(v);
   return fmaxf(v, __shfl_xor(v, 16, 64));
 }
 
@@ -572,15 +575,26 @@ __global__ __launch_bounds__(NT, 1) void k_mx256(MoeArgs p, const int32_t *meta,
   __shared__ __attribute__((aligned(16))) uint8_t scs[2][2 * TM * 16];   // [chunk & 1][row][16]
   __shared__ float s_w[TM];
 
-  const int tile = blockIdx.y;
-  if (tile >= meta[0]) return;
-  const int e = tile_e[tile], r0 = tile_r[tile], nrows = tile_n[tile];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1, h = lane >> 5, l32 = lane & 31;
   const int H = p.H, I = p.I;
   const int K = GU ? H : I;
-  const int c0 = blockIdx.x * (GU ? TN / 2 : TN);   // first h column / hidden column
+  // One workgroup per CU, each walking a list of (tile, column block)
+  // items: workgroup w runs on XCD w % 8, and XCD x takes the x-th eighth
+  // of the expert-ordered tile list, all column blocks of a tile next to
+  // each other.  The 32 workgroups of an XCD then work on the same few row
+  // tiles (which share gathered rows) of the same few experts (whose row
+  // tiles share each weight slab) at once, from that XCD's L2.
+  const int ncol = GU ? I / (TN / 2) : (H + TN - 1) / TN;
+  const int nT = meta[0];
+  const int xcd = blockIdx.x % 8, nslot = ((int)gridDim.x - xcd + 7) / 8;
+  const int lo = (int)((int64_t)nT * xcd / 8), hi = (int)((int64_t)nT * (xcd + 1) / 8);
+  const int items = (hi - lo) * ncol;
+  for (int item = blockIdx.x / 8; item < items; item += nslot) {
+  const int tile = lo + item / ncol;
+  const int e = tile_e[tile], r0 = tile_r[tile], nrows = tile_n[tile];
+  const int c0 = (item % ncol) * (GU ? TN / 2 : TN);   // first h column / hidden column
 
   // A: gathered token rows (gate/up) or sorted h rows (down); rows past the
   // tile read its first row (never stored).  B: gate rows c0.., then up rows
@@ -709,34 +723,37 @@ __global__ __launch_bounds__(NT, 1) void k_mx256(MoeArgs p, const int32_t *meta,
   wait_vmcnt<0>();
 
   if constexpr (GU) {
-    // h = silu(g) * u; the MXFP8 block of 32 h columns is a wave's 32 lanes
+    // h = silu(g) * u; the MXFP8 block of 32 h columns is a wave's 32 lanes.
+    // All 32 values of a lane go through each step together (no branch per
+    // value), so the cross-lane maxima and conversions overlap.
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
       const int col = c0 + wn * 64 + 32 * jj + l32;
+      float hv[16], am[16];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+        for (int r = 0; r < 16; ++r) {
+          const float g = acc[i][jj][r], u = acc[i][jj + 2][r];
+          hv[r] = g * __builtin_amdgcn_rcpf(1.0f + expf(-g)) * u;
+          am[r] = row_max16(fabsf(hv[r]));
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) am[r] = fmaxf(am[r], __shfl_xor(am[r], 16, 64));
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = wm * 64 + i * 32 + acc_row(r, lane);
-          const float g = acc[i][jj][r], u = acc[i][jj + 2][r];
-          const float hv = (g / (1.0f + expf(-g))) * u;
-          const float amax = max32_lanes(fabsf(hv));
-          uint32_t sbyte, code;
-          if (amax == 0.0f) {
-            sbyte = 0u;
-            code = 0u;
-          } else {
-            int X = (int)((__builtin_bit_cast(uint32_t, amax) >> 23) & 0xFF) - 127 - 8;
-            X = X < -127 ? -127 : (X > 127 ? 127 : X);
-            sbyte = (uint32_t)(X + 127);
-            code = f32_to_e4m3_rne_sat(__builtin_ldexpf(hv, -X));
-          }
+          const float amax = am[r];
+          int X = (int)((__builtin_bit_cast(uint32_t, amax) >> 23) & 0xFF) - 127 - 8;
+          X = X < -127 ? -127 : (X > 127 ? 127 : X);
+          const uint32_t sbyte = (uint32_t)(X + 127);   // 0 when amax == 0
+          const uint32_t code = amax == 0.0f ? 0u : f32_to_e4m3_rne_sat(__builtin_ldexpf(hv[r], -X));
           if (row < nrows) {
             const int64_t srow2 = r0 + row;
             if (p.dbg_gu) {
               float *d = p.dbg_gu + (int64_t)sorted[srow2] * (2 * I);
-              d[col] = g;
-              d[I + col] = u;
+              d[col] = acc[i][jj][r];
+              d[I + col] = acc[i][jj + 2][r];
             }
             hq[srow2 * I + col] = (uint8_t)code;
             if (l32 == 0) hs[srow2 * (I / 32) + col / 32] = (uint8_t)sbyte;
@@ -766,6 +783,9 @@ __global__ __launch_bounds__(NT, 1) void k_mx256(MoeArgs p, const int32_t *meta,
           if (n < H) yrow[n] = acc[i][j][r] * w;
         }
       }
+  }
+  // the next item's first loads reuse the slots and the scale buffer
+  __syncthreads();
   }
 }
 
@@ -1211,6 +1231,17 @@ __global__ __launch_bounds__(1024) void k_route_small(const int32_t *ids, const 
 // the decode-sized kernels serve up to 32 tokens when both K dimensions are
 // whole stages (an expert then has at most 32 rows unless a token names it
 // twice; such rows are taken 32 at a time)
+static int moe_cu_count() {
+  static const int n = [] {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      return 256;
+    return cus;
+  }();
+  return n;
+}
+
 // the 256 x 256 grouped GEMMs: scale rows in 16-byte chunks (H, I multiples
 // of 512), 128 h columns per gate/up tile, and every row offset of an
 // operand within 32 bits
@@ -1314,10 +1345,11 @@ hipError_t launch_moe(const MoeArgs &p, hipStream_t stream) {
   hipLaunchKernelGGL(k_scatter, dim3(rb), dim3(256), 0, stream, p.ids, p.tw, L.R, offs, pos, sorted,
                      wsorted);
   if (big) {
-    const dim3 g2(p.I / (t2::TN / 2), L.maxtiles), d2((p.H + t2::TN - 1) / t2::TN, L.maxtiles);
-    hipLaunchKernelGGL(t2::k_mx256<true>, g2, dim3(t2::NT), 0, stream, p, meta, sorted, wsorted,
+    // one workgroup per CU (the kernels walk their items)
+    const dim3 grid(moe_cu_count());
+    hipLaunchKernelGGL(t2::k_mx256<true>, grid, dim3(t2::NT), 0, stream, p, meta, sorted, wsorted,
                        tile_e, tile_r, tile_n, hq, hs, y);
-    hipLaunchKernelGGL(t2::k_mx256<false>, d2, dim3(t2::NT), 0, stream, p, meta, sorted, wsorted,
+    hipLaunchKernelGGL(t2::k_mx256<false>, grid, dim3(t2::NT), 0, stream, p, meta, sorted, wsorted,
                        tile_e, tile_r, tile_n, hq, hs, y);
     hipLaunchKernelGGL(k_combine, dim3((unsigned)((TH4 + 255) / 256)), dim3(256), 0, stream, y,
                        pos, p.T, p.H, p.topk, p.out);

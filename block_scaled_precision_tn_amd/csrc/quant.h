@@ -5,20 +5,21 @@
 
 namespace mg {
 
-// FP32 -> E4M3-FN byte, nearest even, saturating at +-448 (NaN -> 0x7F)
+// FP32 -> E4M3-FN byte, nearest even, saturating at +-448 (NaN -> 0x7F).
+// Written with selects only, so that a wave converting many values runs
+// them back to back: below 2^-6 the code is the value in steps of 2^-9
+// (8 is the smallest normal, code 0x08); above, the FP32 bits rounded to 3
+// mantissa bits with the exponent rebased.
 __device__ __forceinline__ uint32_t f32_to_e4m3_rne_sat(float v) {
   const uint32_t u = __builtin_bit_cast(uint32_t, v);
   const uint32_t sign = (u >> 24) & 0x80u;
   const uint32_t au = u & 0x7FFFFFFFu;
-  if (au > 0x7F800000u) return 0x7Fu;
   const float a = __builtin_bit_cast(float, au);
-  if (!(a < 448.0f)) return sign | 0x7Eu;
-  if (a < 0.015625f) {                   // below 2^-6: steps of 2^-9
-    const uint32_t m = (uint32_t)__builtin_rintf(a * 512.0f);
-    return sign | m;                      // m == 8 is the smallest normal, code 0x08
-  }
-  const uint32_t r = (au + 0x7FFFFu + ((au >> 20) & 1u)) >> 20;  // 8-bit exp | 3-bit mantissa
-  return sign | (r - (120u << 3));
+  const uint32_t sub = (uint32_t)__builtin_rintf(fminf(a, 0.015625f) * 512.0f);
+  const uint32_t nrm = ((au + 0x7FFFFu + ((au >> 20) & 1u)) >> 20) - (120u << 3);
+  uint32_t c = a < 0.015625f ? sub : nrm;
+  c = a < 448.0f ? c : 0x7Eu;
+  return au > 0x7F800000u ? 0x7Fu : (sign | c);
 }
 
 // FP32 -> E2M1 code (sign in bit 3): the nearest of the magnitudes {0, .5, 1,
