@@ -724,8 +724,11 @@ __global__ __launch_bounds__(NT, 1) void k_mx256(MoeArgs p, const int32_t *meta,
 
   if constexpr (GU) {
     // h = silu(g) * u; the MXFP8 block of 32 h columns is a wave's 32 lanes.
-    // All 32 values of a lane go through each step together (no branch per
-    // value), so the cross-lane maxima and conversions overlap.
+    // A lane's 16 values of one block row go through each step together (no
+    // branch per value), so the cross-lane maxima and conversions overlap;
+    // silu takes the hardware exp2 and reciprocal (a few FP32 ulp, far inside
+    // the accumulation tolerance that the re-quantisation check allows), the
+    // codes the clamped hardware converter (bit-identical to the encoder).
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
@@ -735,19 +738,31 @@ __global__ __launch_bounds__(NT, 1) void k_mx256(MoeArgs p, const int32_t *meta,
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float g = acc[i][jj][r], u = acc[i][jj + 2][r];
-          hv[r] = g * __builtin_amdgcn_rcpf(1.0f + expf(-g)) * u;
+          hv[r] = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
           am[r] = row_max16(fabsf(hv[r]));
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) am[r] = fmaxf(am[r], __shfl_xor(am[r], 16, 64));
+        uint32_t sbytes[16], codes[16];
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          int X[2];
+          float v[2];
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            X[q] = (int)((__builtin_bit_cast(uint32_t, am[r + q]) >> 23) & 0xFF) - 127 - 8;
+            X[q] = X[q] < -127 ? -127 : (X[q] > 127 ? 127 : X[q]);
+            sbytes[r + q] = (uint32_t)(X[q] + 127);   // 0 when amax == 0
+            v[q] = __builtin_ldexpf(hv[r + q], -X[q]);
+          }
+          const uint32_t c2 = f32x2_to_e4m3_rne_sat(v[0], v[1]);
+          codes[r] = am[r] == 0.0f ? 0u : (c2 & 0xFFu);
+          codes[r + 1] = am[r + 1] == 0.0f ? 0u : (c2 >> 8);
+        }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = wm * 64 + i * 32 + acc_row(r, lane);
-          const float amax = am[r];
-          int X = (int)((__builtin_bit_cast(uint32_t, amax) >> 23) & 0xFF) - 127 - 8;
-          X = X < -127 ? -127 : (X > 127 ? 127 : X);
-          const uint32_t sbyte = (uint32_t)(X + 127);   // 0 when amax == 0
-          const uint32_t code = amax == 0.0f ? 0u : f32_to_e4m3_rne_sat(__builtin_ldexpf(hv[r], -X));
+          const uint32_t sbyte = sbytes[r], code = codes[r];
           if (row < nrows) {
             const int64_t srow2 = r0 + row;
             if (p.dbg_gu) {
