@@ -46,8 +46,7 @@
 namespace mg {
 namespace {
 
-constexpr int DN = 64;         // weight rows per workgroup
-constexpr int MAXM = 64;       // tokens per launch (two blocks of 32)
+constexpr int MAXM = 128;      // tokens per launch (up to four blocks of 32)
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -79,18 +78,22 @@ __device__ __forceinline__ u32x4 widen8_exact(uint32_t w, float s) {
 
 // R > 0: the power-of-two widening with R live accumulator registers per
 // lane (R = 1: one token, 4: up to 8, 8: up to 16); R = 0: exact widening,
-// TB token blocks of 32.  WIDE: K % (256 or 128) == 0, so each lane
-// fetches the scale bytes of its whole range with one 16- or 8-byte load.
-// Dynamic LDS: max(rows * TROW, TB * 8192) bytes.
-template <int R, int TB, bool WIDE>
-__global__ __launch_bounds__(256) void w4a16_dec_kernel(Bf16Args p, int ks, float *part) {
+// TB token blocks of 32.  NB blocks of 32 weight rows per workgroup (2 NB
+// waves: NB blocks x the two halves of the range); more rows per workgroup
+// spread the token rows it stages over more weight rows.  WIDE: K % (256 or
+// 128) == 0, so each lane fetches the scale bytes of its whole range with
+// one 16- or 8-byte load.  Dynamic LDS: max(rows * TROW, NB * TB * 4096)
+// bytes.
+template <int R, int TB, bool WIDE, int NB>
+__global__ __launch_bounds__(128 * NB) void w4a16_dec_kernel(Bf16Args p, int ks, float *part) {
   constexpr int DK = range_of(R > 0 ? 16 : 17);
   constexpr int HK = DK / 2, CH = HK / 64, TROW = 2 * DK + 16, CPR = DK / 8;
   constexpr int LIVE = R > 0 ? R : 16;   // accumulator registers that can hold tokens
+  constexpr int NW = 2 * NB, DN = 32 * NB;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
-  const int blk = wave & 1, kh = wave >> 1;
+  const int blk = wave % NB, kh = wave / NB;
   const int nt = blockIdx.x / ks, kc = blockIdx.x % ks;
   const int n0 = nt * DN, k0 = kc * DK;
   const int klen = p.K - k0 < DK ? p.K - k0 : DK;   // a multiple of 32
@@ -101,7 +104,7 @@ __global__ __launch_bounds__(256) void w4a16_dec_kernel(Bf16Args p, int ks, floa
   // their own lane instead (they meet zero weights, and zero keeps the
   // products finite)
   int dma = 0;
-  for (int j = wave; j < rows * (CPR / 64); j += 4, ++dma) {
+  for (int j = wave; j < rows * (CPR / 64); j += NW, ++dma) {
     const int t = j / (CPR / 64), c = (j % (CPR / 64)) * 64 + lane;
     uint8_t *dst = lds + t * TROW + 1024 * (j % (CPR / 64));
     if (8 * c < klen)
@@ -270,31 +273,34 @@ __global__ __launch_bounds__(256) void w4a16_dec_reduce(Bf16Args p, int ks, cons
     ((uint16_t *)p.C)[i] = (uint16_t)f32_to_bf16_rne(v);
 }
 
-template <int R, int TB, bool WIDE>
+template <int R, int TB, bool WIDE, int NB>
 hipError_t launch_one(const Bf16Args &p, int ks, float *part, hipStream_t stream) {
-  constexpr int DK = range_of(R > 0 ? 16 : 17), TROW = 2 * DK + 16;
+  constexpr int DK = range_of(R > 0 ? 16 : 17), TROW = 2 * DK + 16, DN = 32 * NB;
+  constexpr int XCH = NB * TB * 4096;   // the range halves' exchange
+  constexpr int MAXL = 32 * TB * TROW > XCH ? 32 * TB * TROW : XCH;
   const int rows = p.M < 32 * TB ? p.M : 32 * TB;
-  const size_t lds = (size_t)(rows * TROW > TB * 8192 ? rows * TROW : TB * 8192);
-  if constexpr (32 * TB * TROW > 65536) {
+  const size_t lds = (size_t)(rows * TROW > XCH ? rows * TROW : XCH);
+  if constexpr (MAXL > 65536) {
     // more than the default 64 KiB of dynamic LDS (gfx950 has 160 KiB per CU)
     static const hipError_t attr =
-        hipFuncSetAttribute((const void *)w4a16_dec_kernel<R, TB, WIDE>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 32 * TB * TROW);
+        hipFuncSetAttribute((const void *)w4a16_dec_kernel<R, TB, WIDE, NB>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, MAXL);
     if (attr != hipSuccess) return attr;
   }
   const dim3 grid((unsigned)(((p.N + DN - 1) / DN) * ks));
-  hipLaunchKernelGGL((w4a16_dec_kernel<R, TB, WIDE>), grid, dim3(256), lds, stream, p, ks, part);
+  hipLaunchKernelGGL((w4a16_dec_kernel<R, TB, WIDE, NB>), grid, dim3(128 * NB), lds, stream, p, ks,
+                     part);
   const int64_t mn = (int64_t)p.M * p.N;
   hipLaunchKernelGGL(w4a16_dec_reduce, dim3((unsigned)((mn + 255) / 256)), dim3(256), 0, stream, p,
                      ks, (const float *)part, R > 0 ? 2.0f : 1.0f);
   return hipGetLastError();
 }
 
-template <int R, int TB>
+template <int R, int TB, int NB = 2>
 hipError_t launch_sel(const Bf16Args &p, int ks, float *part, hipStream_t stream) {
   constexpr int CH = range_of(R > 0 ? 16 : 17) / 128;
-  if ((p.K / 16) % (2 * CH) == 0) return launch_one<R, TB, true>(p, ks, part, stream);
-  return launch_one<R, TB, false>(p, ks, part, stream);
+  if ((p.K / 16) % (2 * CH) == 0) return launch_one<R, TB, true, NB>(p, ks, part, stream);
+  return launch_one<R, TB, false, NB>(p, ks, part, stream);
 }
 
 }  // namespace
@@ -323,8 +329,10 @@ hipError_t launch_w4a16_dec(const Bf16Args &p0, void *ws, hipStream_t stream) {
       e = launch_sel<8, 1>(p, ks, part, stream);
     else if (p.M <= 32)
       e = launch_sel<0, 1>(p, ks, part, stream);
-    else
+    else if (p.M <= 64)
       e = launch_sel<0, 2>(p, ks, part, stream);
+    else   // 128 weight rows per workgroup: the 128 staged token rows serve twice the weight
+      e = launch_sel<0, 4, 4>(p, ks, part, stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

@@ -143,8 +143,8 @@ int mgemm_bf16(const void *A, const void *W, void *C, int64_t M, int64_t N,
    to BF16 in registers (exact: at most 6 significant bits) and run on the
    BF16 MFMA; Sw is applied in the epilogue (hardware::exec docs, module
    description: BF16 activations take the BF16 MMA with the weight widened).
-   Up to 128 tokens take a decode kernel that streams the weight once per 64
-   tokens and splits K over workgroups: each writes FP32 partial sums to
+   Up to 128 tokens take a decode kernel that streams the weight once and
+   splits K over workgroups: each writes FP32 partial sums to
    `ws`, and a second kernel adds them in split order (results are
    run-to-run bit-identical).  `ws` is device memory of at least
    mgemm_workspace_bytes(MGEMM_OP_W4A16, M, N, K, ...) bytes, 16-byte

@@ -101,7 +101,7 @@ def test_workspace_sizes(lib):
     # W4A16: the split-K partials (14 splits of 1024 up to 16 tokens, 28 of
     # 512 above; 64 rows at a time) through 128 tokens, nothing above
     for M, ks in ((1, 14), (16, 14), (17, 28), (64, 28), (128, 28)):
-        assert mg.mgemm_workspace_bytes(mg.OP_W4A16, M, 5376, 14336) == ks * min(M, 64) * 5376 * 4
+        assert mg.mgemm_workspace_bytes(mg.OP_W4A16, M, 5376, 14336) == ks * min(M, 128) * 5376 * 4
     assert mg.mgemm_workspace_bytes(mg.OP_W4A16, 129, 5376, 14336) == 0
     for M in (1, 8, 32, 128):
         assert mg.mgemm_workspace_bytes(mg.OP_W4A8, M, 5376, 14336) > 5376 * 4 * M

@@ -2,10 +2,10 @@
 that streams NVFP4 weights, widens them to BF16 in registers and splits K
 over workgroups) against the FP64 oracle, through the C ABI.
 
-Shapes cover one and two 32-token blocks, the 64-token launch boundary
-(65 and 128 tokens take two launches), the switch to the tiled kernel above
-128 tokens, partial last K ranges, K/16 not a multiple of 16, N not a
-multiple of the 64-row tile, and a K that fits one range (no split).  The
+Shapes cover one, two and four 32-token blocks (65 to 128 tokens: one
+launch on 128-row weight tiles), the switch to the tiled kernel above 128
+tokens, partial last K ranges, K/16 not a multiple of 16, N not a multiple
+of the 64- or 128-row tile, and a K that fits one range (no split).  The
 full-size cases are the workload the bench times: K = 14336, N = 5376,
 M in {1, 16, 128}.
 """
@@ -32,8 +32,8 @@ def test_w4a16_identity_decode_probe():
     """A = identity rows (BF16 1.0), S_w = 1: the FP32 output is each weight
     element e2m1 * e4m3 exactly, for every code byte and every non-NaN scale
     byte (negative and subnormal ones included), through each of the decode
-    kernel's widening forms (1 token, up to 8, up to 16, up to 64 per launch,
-    two launches), so the in-register widening and its K order are bit-exact."""
+    kernel's widening forms (1 token, up to 8, up to 16, up to 64, up to 128
+    tokens), so the in-register widening and its K order are bit-exact."""
     from gpu_cases import gpu_w4a16
     rng = np.random.default_rng(21)
     N, K = 200, 256
