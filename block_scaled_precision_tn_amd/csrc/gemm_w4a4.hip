@@ -340,16 +340,127 @@ __global__ __launch_bounds__(512, 1) void w4a4_fp8route_big(W4A4Args p) {
   }
 }
 
+// The same route on a 256 x 224 tile: 8 waves (8 x 1) of 32 x 224 (1 x 7
+// blocks, 112 accumulator registers); per group a wave reads 1 A and 7 W
+// code operands and 1 + 7 scale operands for 7 blocks.  For shapes whose
+// 256 x 256 grid leaves a partial last round (N = 5376 and M = 8192: 672
+// tiles = 2.6 rounds of 256 CUs) the 224-wide grid can fill whole rounds
+// (768 tiles = 3 rounds, each tile 7/8 of the work).  Staging is the
+// 256 x 256 kernel's (W rows 224..255 are staged and not read).  The
+// scheduling groups keep each block's two MFMAs next to its 16 FMAs.
+constexpr int BN7 = 224;
+
+__global__ __launch_bounds__(512, 1) void w4a4_fp8route_n224(W4A4Args p) {
+  __shared__ __attribute__((aligned(16))) Stage lds[2];
+  __shared__ uint64_t zero8;   // the A-side scale operand of lanes h = 1
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, h = lane >> 5;
+  int tm, tn;
+  xcd_tile(blockIdx.x, (p.M + BM - 1) / BM, (p.N + BN7 - 1) / BN7, tm, tn);
+  const int n0 = tn * BN7, m0 = tm * BM;
+  const int G = p.K / 16;
+  const int S = (G + GPS - 1) / GPS;
+
+  f32x16 acc[7];
+#pragma unroll
+  for (int j = 0; j < 7; ++j) acc[j] = f32x16{0};
+  const f32x16 zero = {0};
+
+  auto compute = [&](const Stage &cur) {
+    const uint8_t *pa = cur.code[0] + coff(wave * 32, 0, 0) + 8 * lane;
+    const uint8_t *pw = cur.code[1] + 8 * lane;
+#pragma unroll
+    for (int g = 0; g < GPS; ++g) {
+      __builtin_amdgcn_sched_barrier(0);
+      const uint64_t a = *(const uint64_t *)(pa + g * 512);
+      const uint64_t sa = h ? zero8 : cur.sc[0][g * BM + wave * 32 + l32];
+      uint64_t w[7], sw[7];
+#pragma unroll
+      for (int j = 0; j < 7; ++j) {
+        w[j] = *(const uint64_t *)(pw + (j * GPS + g) * 512);
+        sw[j] = cur.sc[1][g * BM + 32 * j + l32];
+      }
+#pragma unroll
+      for (int j = 0; j < 7; ++j) {
+        const f32x16 c = mfma_fp8(sa, sw[j], zero);
+        const f32x16 pp = mfma_fp8(a, w[j], zero);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[j][r] = __builtin_fmaf(c[r], pp[r], acc[j][r]);
+      }
+#pragma unroll
+      for (int j = 0; j < 7; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+      }
+    }
+  };
+  if (tid == 0) zero8 = 0;
+  StageRegs r0, r1;
+  load_stage(p, m0, n0, 0, G, tid, r0);
+  load_stage(p, m0, n0, GPS, G, tid, r1);
+  store_stage(lds[0], tid, r0, 0, G);
+  __syncthreads();
+  load_stage(p, m0, n0, 2 * GPS, G, tid, r0);
+  for (int s = 0; s < S; s += 2) {
+    // lds[0] holds stage s, r1 stage s+1, r0 stage s+2 (in flight)
+    compute(lds[0]);
+    store_stage(lds[1], tid, r1, (s + 1) * GPS, G);
+    __syncthreads();
+    load_stage(p, m0, n0, (s + 3) * GPS, G, tid, r1);
+    if (s + 1 >= S) break;
+    compute(lds[1]);
+    store_stage(lds[0], tid, r0, (s + 2) * GPS, G);
+    __syncthreads();
+    load_stage(p, m0, n0, (s + 4) * GPS, G, tid, r0);
+  }
+
+  const float gsc = *p.Sa * *p.Sw * 4096.0f;  // c_g lacks the folded 2^6 * 2^6
+#pragma unroll
+  for (int j = 0; j < 7; ++j) {
+    const int col = n0 + j * 32 + l32;
+    if (col >= p.N) continue;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = m0 + wave * 32 + acc_row(r, lane);
+      if (row >= p.M) continue;
+      const float v = acc[j][r] * gsc;
+      if (p.out_f32)
+        ((float *)p.C)[(int64_t)row * p.N + col] = v;
+      else
+        ((uint16_t *)p.C)[(int64_t)row * p.N + col] = (uint16_t)f32_to_bf16_rne(v);
+    }
+  }
+}
+
 }  // namespace big
 
 }  // namespace
+
+static int w4a4_cus() {
+  static const int n = [] {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      return 256;
+    return cus;
+  }();
+  return n;
+}
 
 hipError_t launch_w4a4(const W4A4Args &p, hipStream_t stream) {
   // the 256 x 256 tile for large products; small ones keep the 128 x 128
   // tile (less padding, more workgroups)
   if (p.M > 128 && p.N > 128) {
-    dim3 grid(((p.N + big::BN - 1) / big::BN) * ((p.M + big::BM - 1) / big::BM));
-    hipLaunchKernelGGL(big::w4a4_fp8route_big, grid, dim3(512), 0, stream, p);
+    // tile width 256 or 224: whichever needs fewer rounds x width (one
+    // workgroup per CU, a round's time proportional to the width)
+    const int64_t tm = (p.M + big::BM - 1) / big::BM, cus = w4a4_cus();
+    const int64_t t8 = tm * ((p.N + big::BN - 1) / big::BN), t7 = tm * ((p.N + big::BN7 - 1) / big::BN7);
+    if ((t7 + cus - 1) / cus * 7 < (t8 + cus - 1) / cus * 8) {
+      hipLaunchKernelGGL(big::w4a4_fp8route_n224, dim3((unsigned)t7), dim3(512), 0, stream, p);
+      return hipGetLastError();
+    }
+    hipLaunchKernelGGL(big::w4a4_fp8route_big, dim3((unsigned)t8), dim3(512), 0, stream, p);
     return hipGetLastError();
   }
   dim3 grid(((p.N + BN - 1) / BN) * ((p.M + BM - 1) / BM));

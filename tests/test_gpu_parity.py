@@ -131,6 +131,21 @@ def test_w4a4_parity(M, N, K):
     check_both("w4a4", inp, c64, b64, what=f"w4a4 {M}x{N}x{K}")
 
 
+# Large W4A4 calls take a 256 x 256 or a 256 x 224 tile, whichever fills the
+# device's rounds with less work (256 CUs: 4096 x 4096 takes 256 x 256, one
+# round against two; 1000-wide N and 8192 x 5376 take 256 x 224).  Both are
+# bit-exact against the route emulation at sampled outputs (corners included).
+@pytest.mark.parametrize("M,N,K", [(4096, 4096, 256), (520, 1000, 544), (1024, 5376, 512)])
+def test_w4a4_tile_widths(M, N, K):
+    from gpu_cases import check_both, oracle_points
+    inp = _w4a4_inputs(M, N, K, seed=M + N)
+    rng = np.random.default_rng(M)
+    m = np.concatenate([[0, 0, M - 1, M - 1, 255, 256], rng.integers(0, M, 400)]).astype(np.int64)
+    n = np.concatenate([[0, N - 1, 0, N - 1, 223, 224], rng.integers(0, N, 400)]).astype(np.int64)
+    c64, b64 = oracle_points("w4a4", inp, m, n)
+    check_both("w4a4", inp, c64, b64, m=m, n=n, what=f"w4a4 {M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("M,N,K", SHAPES)
 def test_bf16_parity(M, N, K):
     from gpu_cases import check_both, oracle_full
