@@ -676,8 +676,12 @@ __global__ __launch_bounds__(NT, 1) void k_mx256(MoeArgs p, const int32_t *meta,
       if (j + 1 < 4) fb[(j + 1) & 1] = frag(lb, bsel[j + 1] + l32, kk);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        acc[i][j] = kk == 0 ? mfma_mx<0>(fa[i], fb[j & 1], acc[i][j], sa[i], sb[j])
-                            : mfma_mx<2>(fa[i], fb[j & 1], acc[i][j], sa[i], sb[j]);
+        if constexpr (GU)   // weight rows on the A side (see the epilogue)
+          acc[i][j] = kk == 0 ? mfma_mx<0>(fb[j & 1], fa[i], acc[i][j], sb[j], sa[i])
+                              : mfma_mx<2>(fb[j & 1], fa[i], acc[i][j], sb[j], sa[i]);
+        else
+          acc[i][j] = kk == 0 ? mfma_mx<0>(fa[i], fb[j & 1], acc[i][j], sa[i], sb[j])
+                              : mfma_mx<2>(fa[i], fb[j & 1], acc[i][j], sa[i], sb[j]);
     }
     __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // fa[0], fa[1], fb[0], fb[1]
 #pragma unroll
@@ -723,65 +727,71 @@ __global__ __launch_bounds__(NT, 1) void k_mx256(MoeArgs p, const int32_t *meta,
   wait_vmcnt<0>();
 
   if constexpr (GU) {
-    // h = silu(g) * u; the MXFP8 block of 32 h columns is a wave's 32 lanes.
-    // A lane's 16 values of one block row go through each step together (no
-    // branch per value), so the cross-lane maxima and conversions overlap;
-    // silu takes the hardware exp2 and reciprocal (a few FP32 ulp, far inside
-    // the accumulation tolerance that the re-quantisation check allows), the
-    // codes the clamped hardware converter (bit-identical to the encoder).
+    // The gate/up MFMAs take the weight rows as their A operand and the
+    // routed rows as B, so a lane's accumulators are one routed row (the
+    // lane's column, l32) by 16 h columns: 8q + 4h + (0..3), q = 0..3, of
+    // each 32-column block, the other 16 in lane ^ 32.
+    // h = silu(g) * u; an MXFP8 block of 32 h columns of one routed row is
+    // 16 values of this lane and 16 of lane ^ 32, so its maximum is taken
+    // in registers and one exchange.  silu takes the hardware exp2 and
+    // reciprocal (a few FP32 ulp, far inside the accumulation tolerance that
+    // the re-quantisation check allows), the codes the clamped hardware
+    // converter (bit-identical to the encoder); 4 adjacent codes are one
+    // dword store.
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-      const int col = c0 + wn * 64 + 32 * jj + l32;
-      float hv[16], am[16];
+        const int t = wm * 64 + i * 32 + l32;   // tile row of this lane
+        const int cb = c0 + wn * 64 + 32 * jj;  // first h column of the block
+        float hv[16];
+        float am = 0.0f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float g = acc[i][jj][r], u = acc[i][jj + 2][r];
           hv[r] = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
-          am[r] = row_max16(fabsf(hv[r]));
+          am = fmaxf(am, fabsf(hv[r]));
         }
+        am = fmaxf(am, __shfl_xor(am, 32, 64));
+        int X = (int)((__builtin_bit_cast(uint32_t, am) >> 23) & 0xFF) - 127 - 8;
+        X = X < -127 ? -127 : (X > 127 ? 127 : X);
+        const uint32_t sbyte = (uint32_t)(X + 127);   // 0 when amax == 0
+        uint32_t w4[4];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) am[r] = fmaxf(am[r], __shfl_xor(am[r], 16, 64));
-        uint32_t sbytes[16], codes[16];
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          int X[2];
-          float v[2];
-#pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            X[q] = (int)((__builtin_bit_cast(uint32_t, am[r + q]) >> 23) & 0xFF) - 127 - 8;
-            X[q] = X[q] < -127 ? -127 : (X[q] > 127 ? 127 : X[q]);
-            sbytes[r + q] = (uint32_t)(X[q] + 127);   // 0 when amax == 0
-            v[q] = __builtin_ldexpf(hv[r + q], -X[q]);
-          }
-          const uint32_t c2 = f32x2_to_e4m3_rne_sat(v[0], v[1]);
-          codes[r] = am[r] == 0.0f ? 0u : (c2 & 0xFFu);
-          codes[r + 1] = am[r + 1] == 0.0f ? 0u : (c2 >> 8);
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t lo = f32x2_to_e4m3_rne_sat(__builtin_ldexpf(hv[4 * q], -X),
+                                                    __builtin_ldexpf(hv[4 * q + 1], -X));
+          const uint32_t hi = f32x2_to_e4m3_rne_sat(__builtin_ldexpf(hv[4 * q + 2], -X),
+                                                    __builtin_ldexpf(hv[4 * q + 3], -X));
+          w4[q] = am == 0.0f ? 0u : ((lo & 0xFFFFu) | (hi << 16));
         }
+        if (t < nrows) {
+          const int64_t srow2 = r0 + t;
+          uint8_t *dq = hq + srow2 * I + cb + 4 * h;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = wm * 64 + i * 32 + acc_row(r, lane);
-          const uint32_t sbyte = sbytes[r], code = codes[r];
-          if (row < nrows) {
-            const int64_t srow2 = r0 + row;
+          for (int q = 0; q < 4; ++q) *(uint32_t *)(dq + 8 * q) = w4[q];
+          if (h == 0) hs[srow2 * (I / 32) + cb / 32] = (uint8_t)sbyte;
+          if (p.dbg_gu || p.dbg_h) {
+            const int64_t ent = sorted[srow2];
             if (p.dbg_gu) {
-              float *d = p.dbg_gu + (int64_t)sorted[srow2] * (2 * I);
-              d[col] = acc[i][jj][r];
-              d[I + col] = acc[i][jj + 2][r];
+              float *d = p.dbg_gu + ent * (2 * I) + cb;
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                d[acc_row(r, lane)] = acc[i][jj][r];
+                d[I + acc_row(r, lane)] = acc[i][jj + 2][r];
+              }
             }
-            hq[srow2 * I + col] = (uint8_t)code;
-            if (l32 == 0) hs[srow2 * (I / 32) + col / 32] = (uint8_t)sbyte;
             if (p.dbg_h) {
-              const int64_t ent = sorted[srow2];
               uint8_t *d = p.dbg_h + ent * (int64_t)(I + I / 32);
-              d[col] = (uint8_t)code;
-              if (l32 == 0) d[I + col / 32] = (uint8_t)sbyte;
+#pragma unroll
+              for (int q = 0; q < 4; ++q) *(uint32_t *)(d + cb + 4 * h + 8 * q) = w4[q];
+              if (h == 0) d[I + cb / 32] = (uint8_t)sbyte;
             }
           }
         }
-    }
+      }
   } else {
+    // routed rows on the A side: a lane holds one y column (l32) of 16 rows
     if (tid < TM) s_w[tid] = wrow;
     __syncthreads();
 #pragma unroll
