@@ -666,14 +666,18 @@ __global__ __launch_bounds__(NT, 1) void k_mx256(MoeArgs p, const int32_t *meta,
   };
   // one K-step: the two A fragments, then the B fragments one block column
   // ahead of the MFMAs that use them, so LDS reads and MFMAs interleave
+  // One K-step: the first MFMA's two fragments are read first (with the
+  // stage's scale dwords in K-step 0), the other A fragment and the second
+  // B fragment next; each later B fragment is read into the register pair
+  // the MFMAs two block columns back have finished with.
   auto kstep = [&](const uint8_t *la, const uint8_t *lb, int kk) {
     i32x8 fa[2], fb[2];
     fa[0] = frag(la, wm * 64 + l32, kk);
-    fa[1] = frag(la, wm * 64 + 32 + l32, kk);
     fb[0] = frag(lb, bsel[0] + l32, kk);
+    fa[1] = frag(la, wm * 64 + 32 + l32, kk);
+    fb[1] = frag(lb, bsel[1] + l32, kk);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      if (j + 1 < 4) fb[(j + 1) & 1] = frag(lb, bsel[j + 1] + l32, kk);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
         if constexpr (GU)   // weight rows on the A side (see the epilogue)
@@ -682,13 +686,19 @@ __global__ __launch_bounds__(NT, 1) void k_mx256(MoeArgs p, const int32_t *meta,
         else
           acc[i][j] = kk == 0 ? mfma_mx<0>(fa[i], fb[j & 1], acc[i][j], sa[i], sb[j])
                               : mfma_mx<2>(fa[i], fb[j & 1], acc[i][j], sa[i], sb[j]);
+      if (j + 2 < 4) fb[j & 1] = frag(lb, bsel[j + 2] + l32, kk);
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // fa[0], fa[1], fb[0], fb[1]
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      if (j + 2 < 4) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
+    if (kk == 0)
+      __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);               // scales, fa[0], fb[0]
+    else
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);                // fa[0], fb[0]
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);                  // fa[1], fb[1]
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                  // block column 2
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                  // block column 3
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
   };
   // stage s: slot (la, lb) readable (loads landed, every wave past the barrier)
   auto ready = [&]() {
@@ -706,7 +716,6 @@ __global__ __launch_bounds__(NT, 1) void k_mx256(MoeArgs p, const int32_t *meta,
       dma16(srow + 16 * (s / CHK + 1), scs[(s / CHK + 1) & 1] + 1024 * wave);
     if (act) {
       scales(s);
-      __builtin_amdgcn_sched_barrier(0);
       kstep(la, lb, 0);
       __builtin_amdgcn_sched_barrier(0);
       kstep(la, lb, 1);
