@@ -293,8 +293,10 @@ __global__ __launch_bounds__(512, 1) void w4a4_fp8route_big(W4A4Args p) {
 #pragma unroll
       for (int b = 0; b < 8; ++b) {
         const int i = b >> 2, j = b & 3;
+        __builtin_amdgcn_s_setprio(1);   // as in the 224-wide kernel below
         const f32x16 c = mfma_fp8(sa[i], sw[j], zero);
         const f32x16 pp = mfma_fp8(a[i], w[j], zero);
+        __builtin_amdgcn_s_setprio(0);
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(c[r], pp[r], acc[i][j][r]);
       }
@@ -383,15 +385,12 @@ __global__ __launch_bounds__(512, 1) void w4a4_fp8route_n224(W4A4Args p) {
       }
 #pragma unroll
       for (int j = 0; j < 7; ++j) {
+        __builtin_amdgcn_s_setprio(1);
         const f32x16 c = mfma_fp8(sa, sw[j], zero);
         const f32x16 pp = mfma_fp8(a, w[j], zero);
+        __builtin_amdgcn_s_setprio(0);
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[j][r] = __builtin_fmaf(c[r], pp[r], acc[j][r]);
-      }
-#pragma unroll
-      for (int j = 0; j < 7; ++j) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
       }
     }
   };
