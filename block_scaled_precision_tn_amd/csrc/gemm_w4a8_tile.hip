@@ -40,10 +40,12 @@ struct Stage {
   float sw[GPS][BN];                // weight group scales x 64, [group][row]
 };
 
+// Every thread stages the same share of a stage (row tid / 4, group tid % 4
+// of each operand), so no wave carries more of the conversion than another.
 struct StageRegs {
-  u32x4 a;         // one group (16 values) of one token row: row tid / 4, group tid % 4
-  u32x4 w;         // 32 codes (groups 2q, 2q+1) of one weight row (threads < 256)
-  uint32_t s0, s1; // scale bytes of groups (0, 1) and (2, 3) of one weight row (threads < 128)
+  u32x4 a;         // one group (16 values) of one token row
+  u32x2 w;         // the 16 codes of that group of one weight row
+  uint32_t s;      // that weight row's scale byte of the group
 };
 
 // Global loads of one stage: addresses clamped in bounds, nothing selected
@@ -58,19 +60,12 @@ __device__ __forceinline__ void load_stage(const W4A8Args &p, int m0, int n0, in
     r.a = *(const u32x4 *)(p.aq + (int64_t)m * p.K + (int64_t)gs * 16);
   }
   {
-    const int row = (tid & 255) >> 1, q = tid & 1, g = g0 + 2 * q;
+    const int row = tid >> 2, g = g0 + (tid & 3);
     int n = n0 + row;
     n = n < p.N ? n : p.N - 1;
-    const int gs = g < G ? g : G - 2;   // G is even (K % 32 == 0): g < G covers g + 1
-    r.w = *(const u32x4 *)(p.wq + (int64_t)n * (p.K / 2) + (int64_t)gs * 8);
-  }
-  {
-    const int row = tid & 127;
-    int n = n0 + row;
-    n = n < p.N ? n : p.N - 1;
-    const uint16_t *s16 = (const uint16_t *)(p.ws + (int64_t)n * (p.K / 16));
-    r.s0 = s16[(g0 < G ? g0 : G - 2) >> 1];
-    r.s1 = s16[(g0 + 2 < G ? g0 + 2 : G - 2) >> 1];
+    const int gs = g < G ? g : G - 1;
+    r.w = *(const u32x2 *)(p.wq + (int64_t)n * (p.K / 2) + (int64_t)gs * 8);
+    r.s = p.ws[(int64_t)n * (p.K / 16) + gs];
   }
 }
 
@@ -83,22 +78,14 @@ __device__ __forceinline__ void store_stage(Stage &s, int tid, const StageRegs &
     *(uint64_t *)(s.code[0] + coff(row, g, 0)) = e4m3x8_even_odd((uint64_t)v[0] | ((uint64_t)v[1] << 32));
     *(uint64_t *)(s.code[0] + coff(row, g, 1)) = e4m3x8_even_odd((uint64_t)v[2] | ((uint64_t)v[3] << 32));
   }
-  if (tid < 256) {
-    const int row = tid >> 1, q = tid & 1;
-    const u32x4 v = g0 + 2 * q < gend ? r.w : u32x4{0, 0, 0, 0};
-    // dwords: (group 2q, half 0) (2q, 1) (2q+1, 0) (2q+1, 1)
-    *(uint64_t *)(s.code[1] + coff(row, 2 * q, 0)) = nvfp4x8_to_e4m3x8(v[0]);
-    *(uint64_t *)(s.code[1] + coff(row, 2 * q, 1)) = nvfp4x8_to_e4m3x8(v[1]);
-    *(uint64_t *)(s.code[1] + coff(row, 2 * q + 1, 0)) = nvfp4x8_to_e4m3x8(v[2]);
-    *(uint64_t *)(s.code[1] + coff(row, 2 * q + 1, 1)) = nvfp4x8_to_e4m3x8(v[3]);
-  }
-  if (tid < 128) {
-    const uint32_t w = r.s0 | (r.s1 << 16);
-#pragma unroll
-    for (int g = 0; g < GPS; ++g) {
-      const float v = e4m3_x64_to_f32_nan((w >> (8 * g)) & 0xFFu);
-      s.sw[g][tid] = g0 + g < gend ? v : 0.0f;
-    }
+  {
+    const int row = tid >> 2, g = tid & 3;
+    const bool in = g0 + g < gend;
+    const u32x2 v = in ? r.w : u32x2{0, 0};
+    // dwords: (group g, half 0) (g, 1)
+    *(uint64_t *)(s.code[1] + coff(row, g, 0)) = nvfp4x8_to_e4m3x8(v[0]);
+    *(uint64_t *)(s.code[1] + coff(row, g, 1)) = nvfp4x8_to_e4m3x8(v[1]);
+    s.sw[g][row] = in ? e4m3_x64_to_f32_nan(r.s & 0xFFu) : 0.0f;
   }
 }
 
