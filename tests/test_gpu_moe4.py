@@ -159,6 +159,51 @@ def test_moe4_stagewise(T, H, I, E, topk):
     _check_down_combine(inp, d, out, T, H, I, topk, tokens)
 
 
+# more than 1024 routed rows (four-kernel routing, many tiles per expert),
+# a partial last K stage (H = 352: 22 groups) and a partial last column
+# block of the down GEMM (H = 352)
+@pytest.mark.parametrize("T,H,I,E,topk", [(1100, 352, 384, 6, 2), (600, 256, 128, 3, 2)])
+def test_moe4_stagewise_many_tiles(T, H, I, E, topk):
+    inp = synth.moe_nvfp4(T, H, I, E, topk, seed=T + E)
+    out, d = run_moe4(inp, T, H, I, E, topk)
+    tokens = np.unique(np.r_[0, 1, np.arange(0, T, 29), T - 1])
+    nd = _check_requant(inp, d, T, H, I, topk, tokens)
+    assert nd <= max(4, len(tokens) * topk * I // 100), nd
+    _check_down_combine(inp, d, out, T, H, I, topk, tokens)
+
+
+def test_moe4_skewed_routing_many_rows():
+    """One expert takes most of 1400 routed rows (many tiles, the last one
+    ragged), others few or none."""
+    T, H, I, E, topk = 700, 128, 256, 8, 2
+    inp = synth.moe_nvfp4(T, H, I, E, topk, seed=6)
+    rng = np.random.default_rng(6)
+    ids = np.where(rng.random((T, topk)) < 0.8, 3, rng.integers(0, 4, (T, topk))).astype(np.int32)
+    ids[:, 1] = np.where(ids[:, 1] == ids[:, 0], (ids[:, 0] + 1) % 4, ids[:, 1])
+    inp["ids"] = ids
+    out, d = run_moe4(inp, T, H, I, E, topk)
+    tokens = np.arange(0, T, 5)
+    _check_requant(inp, d, T, H, I, topk, tokens)
+    _check_down_combine(inp, d, out, T, H, I, topk, tokens)
+
+
+def test_moe4_routing_paths_agree():
+    """The four-kernel routing and the one-launch routing give the same
+    bits: the same tokens routed as 1040 rows (four kernels) and, in a call
+    of their own, as the first 1024 of them (one launch) -- the tokens of
+    both calls share every expert's weights, and a row's results do not
+    depend on the other rows."""
+    T, H, I, E, topk = 260, 256, 256, 8, 4
+    inp = synth.moe_nvfp4(T, H, I, E, topk, seed=21)
+    out_big, d_big = run_moe4(inp, T, H, I, E, topk)
+    small = dict(inp)
+    small["xq"], small["xs"] = inp["xq"][:256], inp["xs"][:256]
+    small["ids"], small["tw"] = inp["ids"][:256], inp["tw"][:256]
+    out_small, d_small = run_moe4(small, 256, H, I, E, topk)
+    assert np.array_equal(d_big[:256 * topk], d_small), "requantised h differs between routing paths"
+    assert np.array_equal(out_big[:256], out_small), "output differs between routing paths"
+
+
 def test_moe4_skewed_routing_and_empty_experts():
     """Half the experts get no tokens, one gets most (several 128-row tiles)."""
     T, H, I, E, topk = 200, 128, 128, 8, 2
