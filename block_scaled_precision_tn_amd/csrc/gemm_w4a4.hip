@@ -192,6 +192,16 @@ __global__ __launch_bounds__(512, 2) void w4a4_fp8route_kernel(W4A4Args p) {
 // 128 x 128 tile's per block).  One workgroup per CU (2 waves per SIMD; the
 // accumulators of 8 blocks take 128 registers).  Every FP32 rounding is the
 // 128 x 128 kernel's (the same group terms in the same order).
+//
+// Scale operands here come from one word per row and stage: a row's four
+// group scale bytes at K = 0..3 (zeros above).  A W-side lane passes its
+// row's word whole; an A-side lane passes its row's word masked to group g's
+// byte (lanes h = 1, K = 8..15: zero).  The K = 16 MFMA then sums one nonzero
+// product, s_a * s_w of group g, exactly.  The other W bytes meet zeros; only
+// a NaN among them changes the sum (to NaN), and that byte makes its whole
+// output column NaN anyway.  This reads one scale word per block and stage
+// instead of one 8-byte operand per block and group (LDS reads per stage and
+// wave: 39 instead of 64 in the 224-wide kernel).
 namespace big {
 
 constexpr int BM = 256, BN = 256;
@@ -201,7 +211,7 @@ __device__ __forceinline__ int coff(int row, int g, int h) {
 }
 struct Stage {
   uint8_t code[2][BM * GPS * 16];   // A, W codes as E4M3 in MFMA operand order
-  uint64_t sc[2][GPS * BM];         // [g][row]: raw scale byte at K = 0, zeros above
+  uint64_t sc[2][BM];               // [row]: the 4 groups' raw scale bytes at K = 0..3, zeros above
 };
 struct StageRegs {
   u32x4 a, w;        // 32 codes of one A row and one W row (groups 2q, 2q+1)
@@ -247,14 +257,11 @@ __device__ __forceinline__ void store_stage(Stage &s, int tid, const StageRegs &
   store_codes(s.code[0], row, q, in ? r.a : u32x4{0, 0, 0, 0});
   store_codes(s.code[1], row, q, in ? r.w : u32x4{0, 0, 0, 0});
   const uint32_t w = (g0 < G ? r.s0 : 0u) | ((g0 + 2 < G ? r.s1 : 0u) << 16);
-  const int op = tid >> 8, srow = tid & 255;
-#pragma unroll
-  for (int g = 0; g < GPS; ++g) s.sc[op][g * BM + srow] = (w >> (8 * g)) & 0xFFu;
+  s.sc[tid >> 8][tid & 255] = w;   // zero-extended: K = 4..7 of the operand read as 0
 }
 
 __global__ __launch_bounds__(512, 1) void w4a4_fp8route_big(W4A4Args p) {
   __shared__ __attribute__((aligned(16))) Stage lds[2];
-  __shared__ uint64_t zero8;   // the A-side scale operand of lanes h = 1
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, h = lane >> 5;
@@ -271,25 +278,31 @@ __global__ __launch_bounds__(512, 1) void w4a4_fp8route_big(W4A4Args p) {
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{0};
   const f32x16 zero = {0};
 
+  // scale operands (see scale_ops): A-side lanes take their row's word
+  // masked to group g's byte (lanes h = 1: zero), W-side lanes their row's
+  // whole word, so the K = 16 product is exactly s_a * s_w of group g
+  uint32_t amask[GPS];
+#pragma unroll
+  for (int g = 0; g < GPS; ++g) amask[g] = h ? 0u : 0xFFu << (8 * g);
   auto compute = [&](const Stage &cur) {
-    // scale operands: lane (row, h = 0) holds its row's raw scale byte at
-    // K = 0 and zeros elsewhere; A-side lanes h = 1 read zeros, so the K = 16
-    // product is exactly s_a * s_w (a NaN scale still yields NaN)
     const uint8_t *pa = cur.code[0] + coff(wm * 64, 0, 0) + 8 * lane;
     const uint8_t *pw = cur.code[1] + coff(wn * 128, 0, 0) + 8 * lane;
+    uint32_t saw[2];
+    uint64_t sw[4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) saw[i] = (uint32_t)cur.sc[0][wm * 64 + 32 * i + l32];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sw[j] = cur.sc[1][wn * 128 + 32 * j + l32];
 #pragma unroll
     for (int g = 0; g < GPS; ++g) {
-      uint64_t a[2], w[4], sa[2], sw[4];
+      uint64_t a[2], w[4], sa[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         a[i] = *(const uint64_t *)(pa + (i * GPS + g) * 512);
-        sa[i] = h ? zero8 : cur.sc[0][g * BM + wm * 64 + 32 * i + l32];
+        sa[i] = saw[i] & amask[g];
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        w[j] = *(const uint64_t *)(pw + (j * GPS + g) * 512);
-        sw[j] = cur.sc[1][g * BM + wn * 128 + 32 * j + l32];
-      }
+      for (int j = 0; j < 4; ++j) w[j] = *(const uint64_t *)(pw + (j * GPS + g) * 512);
 #pragma unroll
       for (int b = 0; b < 8; ++b) {
         const int i = b >> 2, j = b & 3;
@@ -302,7 +315,6 @@ __global__ __launch_bounds__(512, 1) void w4a4_fp8route_big(W4A4Args p) {
       }
     }
   };
-  if (tid == 0) zero8 = 0;
   StageRegs r0, r1;
   load_stage(p, m0, n0, 0, G, tid, r0);
   load_stage(p, m0, n0, GPS, G, tid, r1);
@@ -357,7 +369,6 @@ constexpr int BN7 = 224;
 
 __global__ __launch_bounds__(512, 1) void w4a4_fp8route_n224(W4A4Args p) {
   __shared__ __attribute__((aligned(16))) Stage lds[2];
-  __shared__ uint64_t zero8;   // the A-side scale operand of lanes h = 1
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
@@ -372,20 +383,24 @@ __global__ __launch_bounds__(512, 1) void w4a4_fp8route_n224(W4A4Args p) {
   for (int j = 0; j < 7; ++j) acc[j] = f32x16{0};
   const f32x16 zero = {0};
 
+  uint32_t amask[GPS];   // as in the 256 x 256 kernel
+#pragma unroll
+  for (int g = 0; g < GPS; ++g) amask[g] = h ? 0u : 0xFFu << (8 * g);
   auto compute = [&](const Stage &cur) {
     const uint8_t *pa = cur.code[0] + coff(wave * 32, 0, 0) + 8 * lane;
     const uint8_t *pw = cur.code[1] + 8 * lane;
+    const uint32_t saw = (uint32_t)cur.sc[0][wave * 32 + l32];
+    uint64_t sw[7];
+#pragma unroll
+    for (int j = 0; j < 7; ++j) sw[j] = cur.sc[1][32 * j + l32];
 #pragma unroll
     for (int g = 0; g < GPS; ++g) {
       __builtin_amdgcn_sched_barrier(0);
       const uint64_t a = *(const uint64_t *)(pa + g * 512);
-      const uint64_t sa = h ? zero8 : cur.sc[0][g * BM + wave * 32 + l32];
-      uint64_t w[7], sw[7];
+      const uint64_t sa = saw & amask[g];
+      uint64_t w[7];
 #pragma unroll
-      for (int j = 0; j < 7; ++j) {
-        w[j] = *(const uint64_t *)(pw + (j * GPS + g) * 512);
-        sw[j] = cur.sc[1][g * BM + 32 * j + l32];
-      }
+      for (int j = 0; j < 7; ++j) w[j] = *(const uint64_t *)(pw + (j * GPS + g) * 512);
 #pragma unroll
       for (int j = 0; j < 7; ++j) {
         __builtin_amdgcn_s_setprio(1);
@@ -397,7 +412,6 @@ __global__ __launch_bounds__(512, 1) void w4a4_fp8route_n224(W4A4Args p) {
       }
     }
   };
-  if (tid == 0) zero8 = 0;
   StageRegs r0, r1;
   load_stage(p, m0, n0, 0, G, tid, r0);
   load_stage(p, m0, n0, GPS, G, tid, r1);

@@ -255,6 +255,30 @@ def test_nan_scale_propagates():
     assert np.array_equal(c1[~nan], c0[~nan])
 
 
+@pytest.mark.parametrize("M,N,K", [(4096, 4096, 256), (520, 1000, 544)])
+def test_nan_scale_propagates_wide_tiles(M, N, K):
+    """The same on the 256 x 256 and 256 x 224 tiles, whose scale operands
+    carry a stage's four group scale bytes at once: NaN bytes in the first
+    and last group of a row or column make exactly that row or column NaN
+    (as the oracle's decode does for any group), the rest stays bit for bit."""
+    from gpu_cases import GPU
+    inp = synth.w4a4(M, N, K, seed=43)
+    G = K // 16
+    c0 = GPU["w4a4"](inp, True)
+    as_ = inp["as_"].copy()
+    as_[3, 5] = 0x7F
+    as_[M - 2, G - 1] = 0xFF
+    ws = inp["ws"].copy()
+    ws[10, 2] = 0xFF
+    ws[N - 1, 0] = 0x7F
+    c1 = GPU["w4a4"](dict(inp, as_=as_, ws=ws), True)
+    nan = np.zeros(c1.shape, bool)
+    nan[[3, M - 2], :] = True
+    nan[:, [10, N - 1]] = True
+    assert np.array_equal(np.isnan(c1), nan)
+    assert np.array_equal(c1[~nan], c0[~nan])
+
+
 # ------------------------------------------------------------------- plan
 def test_plan_on_device():
     import block_scaled_precision_tn_amd as mg
