@@ -356,7 +356,7 @@ __global__ __launch_bounds__(512, 1) void w4a4_fp8route_big(W4A4Args p) {
 
 // The same route on a 256 x 224 tile: 8 waves (8 x 1) of 32 x 224 (1 x 7
 // blocks, 112 accumulator registers); per group a wave reads 1 A and 7 W
-// code operands and 1 + 7 scale operands for 7 blocks.  For shapes whose
+// code operands for 7 blocks, and per stage 1 + 7 scale words.  For shapes whose
 // 256 x 256 grid leaves a partial last round (N = 5376 and M = 8192: 672
 // tiles = 2.6 rounds of 256 CUs) the 224-wide grid can fill whole rounds
 // (768 tiles = 3 rounds, each tile 7/8 of the work).  Staging is the
@@ -364,7 +364,10 @@ __global__ __launch_bounds__(512, 1) void w4a4_fp8route_big(W4A4Args p) {
 // block's two MFMAs are issued at raised wave priority: the wave that
 // reaches its MFMAs gets the issue slot ahead of the other wave's FMAs on
 // the same SIMD, so the matrix unit and the FP32 FMAs overlap more (645-650
-// against 622-627 TFLOP/s at the headline shape without it).
+// against 622-627 TFLOP/s at the headline shape without it).  The scale
+// product of the next block is issued right after the current block's P'_g
+// MFMA (16 more registers, 244 in all), so it runs on the matrix unit while
+// the wave's own FMAs of the current block issue (652-653 against 647).
 constexpr int BN7 = 224;
 
 __global__ __launch_bounds__(512, 1) void w4a4_fp8route_n224(W4A4Args p) {
@@ -393,19 +396,24 @@ __global__ __launch_bounds__(512, 1) void w4a4_fp8route_n224(W4A4Args p) {
     uint64_t sw[7];
 #pragma unroll
     for (int j = 0; j < 7; ++j) sw[j] = cur.sc[1][32 * j + l32];
+    f32x16 cn = mfma_fp8(saw & amask[0], sw[0], zero);
 #pragma unroll
     for (int g = 0; g < GPS; ++g) {
       __builtin_amdgcn_sched_barrier(0);
       const uint64_t a = *(const uint64_t *)(pa + g * 512);
-      const uint64_t sa = saw & amask[g];
       uint64_t w[7];
 #pragma unroll
       for (int j = 0; j < 7; ++j) w[j] = *(const uint64_t *)(pw + (j * GPS + g) * 512);
 #pragma unroll
       for (int j = 0; j < 7; ++j) {
+        const f32x16 c = cn;
         __builtin_amdgcn_s_setprio(1);
-        const f32x16 c = mfma_fp8(sa, sw[j], zero);
         const f32x16 pp = mfma_fp8(a, w[j], zero);
+        __builtin_amdgcn_sched_barrier(0);
+        if (j < 6)
+          cn = mfma_fp8(saw & amask[g], sw[j + 1], zero);
+        else if (g + 1 < GPS)
+          cn = mfma_fp8(saw & amask[g + 1], sw[0], zero);
         __builtin_amdgcn_s_setprio(0);
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[j][r] = __builtin_fmaf(c[r], pp[r], acc[j][r]);
