@@ -293,6 +293,9 @@ __global__ __launch_bounds__(512, 1) void w4a4_fp8route_big(W4A4Args p) {
     for (int i = 0; i < 2; ++i) saw[i] = (uint32_t)cur.sc[0][wm * 64 + 32 * i + l32];
 #pragma unroll
     for (int j = 0; j < 4; ++j) sw[j] = cur.sc[1][wn * 128 + 32 * j + l32];
+    // the next block's scale product is issued after the current block's
+    // P'_g MFMA, as in the 224-wide kernel
+    f32x16 cn = mfma_fp8(saw[0] & amask[0], sw[0], zero);
 #pragma unroll
     for (int g = 0; g < GPS; ++g) {
       uint64_t a[2], w[4], sa[2];
@@ -306,9 +309,14 @@ __global__ __launch_bounds__(512, 1) void w4a4_fp8route_big(W4A4Args p) {
 #pragma unroll
       for (int b = 0; b < 8; ++b) {
         const int i = b >> 2, j = b & 3;
+        const f32x16 c = cn;
         __builtin_amdgcn_s_setprio(1);   // see the 224-wide kernel below
-        const f32x16 c = mfma_fp8(sa[i], sw[j], zero);
         const f32x16 pp = mfma_fp8(a[i], w[j], zero);
+        __builtin_amdgcn_sched_barrier(0);
+        if (b < 7)
+          cn = mfma_fp8(sa[(b + 1) >> 2], sw[(b + 1) & 3], zero);
+        else if (g + 1 < GPS)
+          cn = mfma_fp8(saw[0] & amask[g + 1], sw[0], zero);
         __builtin_amdgcn_s_setprio(0);
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(c[r], pp[r], acc[i][j][r]);
