@@ -9,7 +9,10 @@ per 16, FP32 tensor scales; exact E2M1->E4M3 conversion onto the FP8 MFMA,
 per-16 FP32 scale step, BF16 output), inputs resident in HBM.  W warmup steps
 run untimed, then exactly K steps are timed between two device
 synchronisations with HIP events on the stream the kernel runs on.  `value`
-is TFLOP/s = 2*M*N*K / time per step.
+is TFLOP/s = 2*M*N*K / time per step.  The headline's inputs are uploaded
+first and its steps are timed after the decode and BF16 legs, on a GPU at
+the clock it holds under load; every other leg warms up for WARM_S seconds
+of calls before it is timed.
 
 The same JSON line also carries: the roofline of that kernel, the FP64 CPU
 oracle timed on the host on a bounded sample of the same workload
